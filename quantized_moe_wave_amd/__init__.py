@@ -1,0 +1,18 @@
+"""Routed-expert MoE FFN layer (Q4_K experts) for MI355X / gfx950.
+
+The layer runs in hand-written HIP kernels behind the C ABI of
+include/moe_ffn.h; this package is a thin ctypes binding with the same names.
+"""
+from .binding import (  # noqa: F401
+    MoeError,
+    MoeFfn,
+    abi_version,
+    moe_ffn_create,
+    moe_ffn_debug_routing,
+    moe_ffn_destroy,
+    moe_ffn_forward,
+    moe_ffn_profile,
+    moe_ffn_profile_read,
+    moe_ffn_stage_names,
+    moe_ffn_reserve,
+)

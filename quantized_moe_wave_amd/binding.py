@@ -1,0 +1,205 @@
+"""ctypes binding of the C ABI in include/moe_ffn.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, and their device pointers and the current HIP stream are passed
+through. Every step of the layer runs in the HIP kernels of libmoe_ffn.so;
+there is no other implementation behind these names, and importing this
+module fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB
+
+if not os.path.exists(LIB):
+    raise ImportError(f"{LIB} is missing: build it first (python -m quantized_moe_wave_amd.build)")
+
+_lib = ctypes.CDLL(LIB)
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_SHAPE", 2: "MOE_ERR_INVALID_ARG", 3: "MOE_ERR_BLOB_SIZE",
+                4: "MOE_ERR_DEVICE", 5: "MOE_ERR_OOM"}
+
+
+class MoeFfnShape(ctypes.Structure):
+    _fields_ = [("hidden_dim", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("num_experts_per_tok", ctypes.c_int32), ("moe_intermediate", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_lib.moe_ffn_create.argtypes = [ctypes.POINTER(MoeFfnShape), _vp, ctypes.c_size_t, _vp, ctypes.c_size_t, _vp,
+                                ctypes.c_size_t, _vp, _vp, _vp, ctypes.POINTER(_vp)]
+_lib.moe_ffn_create.restype = ctypes.c_int
+_lib.moe_ffn_reserve.argtypes = [_vp, ctypes.c_int32, _vp]
+_lib.moe_ffn_reserve.restype = ctypes.c_int
+_lib.moe_ffn_forward.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_forward.restype = ctypes.c_int
+_lib.moe_ffn_debug_routing.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_debug_routing.restype = ctypes.c_int
+_lib.moe_ffn_destroy.argtypes = [_vp]
+_lib.moe_ffn_destroy.restype = ctypes.c_int
+_lib.moe_ffn_last_error.argtypes = []
+_lib.moe_ffn_last_error.restype = ctypes.c_char_p
+_lib.moe_ffn_abi_version.argtypes = []
+_lib.moe_ffn_abi_version.restype = ctypes.c_int32
+_lib.moe_ffn_profile.argtypes = [_vp, ctypes.c_uint32]
+_lib.moe_ffn_profile.restype = ctypes.c_int
+_lib.moe_ffn_profile_read.argtypes = [_vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32)]
+_lib.moe_ffn_profile_read.restype = ctypes.c_int
+_lib.moe_ffn_stage_count.argtypes = []
+_lib.moe_ffn_stage_count.restype = ctypes.c_int32
+_lib.moe_ffn_stage_name.argtypes = [ctypes.c_int32]
+_lib.moe_ffn_stage_name.restype = ctypes.c_char_p
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.moe_ffn_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def abi_version() -> int:
+    return int(_lib.moe_ffn_abi_version())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def moe_ffn_create(hidden_dim: int, num_experts: int, num_experts_per_tok: int, moe_intermediate: int,
+                   gate_q4k: torch.Tensor, up_q4k: torch.Tensor, down_q4k: torch.Tensor,
+                   router_w: torch.Tensor, router_bias: torch.Tensor | None = None, stream=None) -> int:
+    """Return an opaque handle (int). Weights: uint8 blobs and fp32 router tensors on the GPU."""
+    for n, t in (("gate_q4k", gate_q4k), ("up_q4k", up_q4k), ("down_q4k", down_q4k)):
+        _dev(t, n, torch.uint8)
+    _dev(router_w, "router_w", torch.float32)
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32)
+    shape = MoeFfnShape(hidden_dim, num_experts, num_experts_per_tok, moe_intermediate)
+    out = _vp()
+    st = _lib.moe_ffn_create(ctypes.byref(shape), _ptr(gate_q4k), gate_q4k.numel(), _ptr(up_q4k), up_q4k.numel(),
+                             _ptr(down_q4k), down_q4k.numel(), _ptr(router_w), _ptr(router_bias), _stream(stream),
+                             ctypes.byref(out))
+    _check(st, "moe_ffn_create")
+    return out.value
+
+
+def moe_ffn_reserve(handle: int, max_tokens: int, stream=None) -> None:
+    _check(_lib.moe_ffn_reserve(_vp(handle), int(max_tokens), _stream(stream)), "moe_ffn_reserve")
+
+
+def moe_ffn_forward(handle: int, x: torch.Tensor, out: torch.Tensor, router_out: torch.Tensor | None = None,
+                    router_idx: torch.Tensor | None = None, stream=None) -> None:
+    """out[T][H] <- MoE FFN of x[T][H]; router_out/router_idx [T][k] optional."""
+    _dev(x, "x", torch.float32)
+    _dev(out, "out", torch.float32)
+    if x.dim() != 2 or out.shape != x.shape:
+        raise ValueError("x and out must both be [T, hidden_dim]")
+    if router_out is not None:
+        _dev(router_out, "router_out", torch.float32)
+    if router_idx is not None:
+        _dev(router_idx, "router_idx", torch.int32)
+    st = _lib.moe_ffn_forward(_vp(handle), int(x.shape[0]), _ptr(x), _ptr(out), _ptr(router_out), _ptr(router_idx),
+                              _stream(stream))
+    _check(st, "moe_ffn_forward")
+
+
+def moe_ffn_debug_routing(handle: int, logits: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                          offsets: torch.Tensor | None = None, entries: torch.Tensor | None = None,
+                          stream=None) -> None:
+    for n, t, dt in (("logits", logits, torch.float64), ("counts", counts, torch.int32),
+                     ("offsets", offsets, torch.int32), ("entries", entries, torch.int32)):
+        if t is not None:
+            _dev(t, n, dt)
+    st = _lib.moe_ffn_debug_routing(_vp(handle), _ptr(logits), _ptr(counts), _ptr(offsets), _ptr(entries),
+                                    _stream(stream))
+    _check(st, "moe_ffn_debug_routing")
+
+
+def moe_ffn_stage_names() -> list[str]:
+    return [_lib.moe_ffn_stage_name(i).decode() for i in range(_lib.moe_ffn_stage_count())]
+
+
+def moe_ffn_profile(handle: int, stages) -> None:
+    """Bracket the named stages (or stage indices) of every forward with HIP events."""
+    names = moe_ffn_stage_names()
+    mask = 0
+    for s in stages:
+        mask |= 1 << (names.index(s) if isinstance(s, str) else int(s))
+    _check(_lib.moe_ffn_profile(_vp(handle), mask), "moe_ffn_profile")
+
+
+def moe_ffn_profile_read(handle: int) -> dict:
+    """{stage name: (total ms, launches)} since the last read."""
+    n = _lib.moe_ffn_stage_count()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int32 * n)()
+    _check(_lib.moe_ffn_profile_read(_vp(handle), ms, cnt), "moe_ffn_profile_read")
+    return {name: (ms[i], cnt[i]) for i, name in enumerate(moe_ffn_stage_names())}
+
+
+def moe_ffn_destroy(handle: int) -> None:
+    _check(_lib.moe_ffn_destroy(_vp(handle)), "moe_ffn_destroy")
+
+
+class MoeFfn:
+    """Owning wrapper: one layer's weights on the GPU plus its workspace."""
+
+    def __init__(self, hidden_dim, num_experts, num_experts_per_tok, moe_intermediate, gate_q4k, up_q4k, down_q4k,
+                 router_w, router_bias=None, stream=None):
+        self.hidden_dim = hidden_dim
+        self.num_experts = num_experts
+        self.top_k = num_experts_per_tok
+        self.moe_intermediate = moe_intermediate
+        self.handle = moe_ffn_create(hidden_dim, num_experts, num_experts_per_tok, moe_intermediate, gate_q4k,
+                                     up_q4k, down_q4k, router_w, router_bias, stream)
+
+    def reserve(self, max_tokens: int, stream=None) -> None:
+        moe_ffn_reserve(self.handle, max_tokens, stream)
+
+    def forward(self, x, out=None, router_out=None, router_idx=None, stream=None):
+        if out is None:
+            out = torch.empty_like(x)
+        moe_ffn_forward(self.handle, x, out, router_out, router_idx, stream)
+        return out
+
+    def close(self) -> None:
+        if self.handle:
+            moe_ffn_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,57 @@
+// Device-side types and helpers shared by the MoE FFN kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef _Float16 f16;
+typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kQ4Bytes = 144;    // bytes of one Q4_K super-block
+constexpr int kQ4Weights = 256;  // weights of one Q4_K super-block
+constexpr int kRowGroup = 16;    // rows per repacked row group (= MFMA N)
+constexpr int kGroupSbBytes = kRowGroup * kQ4Bytes;  // 2304: one row group x one super-block
+constexpr int kGroupQsBytes = 2048;                  // quant part of that block
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;
+constexpr int kTileM = 16;       // tokens per expert tile in the MFMA expert kernel
+
+// Staged activation layout (one row = one token or one expert slot, K = nsb*256):
+//   hilo  : for super-block b, k-step s (32 columns), lane group g (8 columns):
+//           16 halves = 8 "hi" then 8 "lo" values of the scaled row, at half
+//           offset ((b*8 + s)*4 + g)*16. Element e holds column
+//           256b + 32s + 8g + kPerm[e] (the order the Q4_K nibble unpack yields).
+//   xs    : per (row, b) 16 halves: hi of the 8 k-step sums, then their lo.
+//   sinv  : per (row, b) the power of two that undoes the row scaling.
+// kPerm = {0, 2, 1, 3, 4, 6, 5, 7}.
+__device__ __forceinline__ int perm8(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+    return (float)__builtin_bit_cast(f16, (uint16_t)bits16);
+}
+
+__device__ __forceinline__ f16x2 u32_as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t f16x2_as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// Wave-wide reductions (64 lanes).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+}  // namespace moe

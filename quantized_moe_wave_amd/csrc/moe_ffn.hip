@@ -1,0 +1,431 @@
+// Host side of the C ABI declared in include/moe_ffn.h: validation, weight
+// repack, workspace, and the per-call launch sequence.
+//
+// forward(T) enqueues, all on the caller's stream, with no host wait:
+//   1. router_kernel   logits (fp64), top-k, renormalised weights
+//   2. bucket_kernel   stable counting sort of (token, slot) by expert + tiles
+//   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums
+//   4. expert GATEUP   gate/up Q4_K MFMA + SiLU(g)*u -> h[slot][I]
+//   5. stage_kernel    h rows -> staged
+//   6. expert DOWN     down Q4_K MFMA -> Y[slot][H]
+//   7. combine_kernel  out[t] = sum_j w[t][j] * Y[pos[t][j]]
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe_ffn.h"
+#include "bucket.hpp"
+#include "common.hpp"
+#include "expert.hpp"
+#include "repack.hpp"
+#include "router.hpp"
+#include "stage.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                        \
+    do {                                                                                     \
+        hipError_t e_ = (expr);                                                              \
+        if (e_ != hipSuccess)                                                                \
+            return fail(e_ == hipErrorOutOfMemory ? MOE_ERR_OOM : MOE_ERR_DEVICE, "%s: %s (%s)", \
+                        #expr, hipGetErrorString(e_), __func__);                             \
+    } while (0)
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace for up to cap tokens (S = cap * k slots).
+struct Workspace {
+    double *logits = nullptr;     // [T][E]
+    int32_t *idx = nullptr;       // [T][k] (used when the caller passes no router_idx)
+    float *w = nullptr;           // [T][k] (used when the caller passes no router_out)
+    uint32_t *rcount = nullptr;   // [token groups] router completion counters (kept at zero)
+    int32_t *counts = nullptr;    // [E]
+    int32_t *offsets = nullptr;   // [E+1]
+    int32_t *entries = nullptr;   // [S]
+    int32_t *pos = nullptr;       // [S]
+    int4 *tiles = nullptr;        // [max tiles]
+    int32_t *n_tiles = nullptr;   // [1]
+    f16 *x_hilo = nullptr;        // [T][2H]
+    f16 *x_xs = nullptr;          // [T][H/256][16]
+    float *x_sinv = nullptr;      // [T][H/256]
+    float *h = nullptr;           // [S][I]
+    f16 *h_hilo = nullptr;        // [S][2I]
+    f16 *h_xs = nullptr;          // [S][I/256][16]
+    float *h_sinv = nullptr;      // [S][I/256]
+    float *Y = nullptr;           // [S][H]
+};
+
+int max_tiles(int S, int E) { return S / kTileM + std::min(E, S); }
+
+enum Stage { kStRouter = 0, kStBucket, kStStageX, kStGateUp, kStStageH, kStDown, kStCombine, kStCount };
+const char *const kStageNames[kStCount] = {"router", "bucket", "stage_x", "gate_up", "stage_h", "down", "combine"};
+
+// Start/stop events of profiled stages. A profiled kernel is launched with
+// hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
+struct Profiler {
+    uint32_t mask = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> pairs[kStCount];
+    size_t used[kStCount] = {};
+    // Next free event pair of stage s, or {nullptr, nullptr} if s is not profiled.
+    std::pair<hipEvent_t, hipEvent_t> next(int s) {
+        if (!((mask >> s) & 1)) return {nullptr, nullptr};
+        if (used[s] == pairs[s].size()) {
+            hipEvent_t a = nullptr, b = nullptr;
+            if (hipEventCreate(&a) != hipSuccess) return {nullptr, nullptr};
+            if (hipEventCreate(&b) != hipSuccess) {
+                (void)hipEventDestroy(a);
+                return {nullptr, nullptr};
+            }
+            pairs[s].push_back({a, b});
+        }
+        return pairs[s][used[s]++];
+    }
+    ~Profiler() {
+        for (auto &v : pairs)
+            for (auto &p : v) {
+                (void)hipEventDestroy(p.first);
+                (void)hipEventDestroy(p.second);
+            }
+    }
+};
+
+// Launch kernel on st; if stage s is profiled, bracket it with its events.
+template <typename... KArgs, typename... Args>
+void launch(Profiler &pf, int s, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st, Args... args) {
+    auto ev = pf.next(s);
+    if (ev.first)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.first, ev.second, 0, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, 0, st>>>(static_cast<KArgs>(args)...);
+}
+
+}  // namespace
+
+struct moe_ffn_s {
+    moe_ffn_shape sh{};
+    int device = -1;
+    uint8_t *gu = nullptr;   // repacked gate/up
+    uint8_t *dn = nullptr;   // repacked down
+    float *rw = nullptr;     // [E][H]
+    float *rb = nullptr;     // [E] or null
+    void *ws_base = nullptr;
+    int cap = 0;             // tokens the workspace holds
+    Workspace ws;
+    int last_T = 0;
+    Profiler prof;
+};
+
+namespace {
+
+bool is_device_ptr(const void *p) {
+    if (!p) return false;
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged;
+}
+
+moe_status check_shape(const moe_ffn_shape *s) {
+    if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    const int H = s->hidden_dim, E = s->num_experts, k = s->num_experts_per_tok, I = s->moe_intermediate;
+    if (E <= 0 || k <= 0 || I <= 0)
+        return fail(MOE_ERR_INVALID_SHAPE,
+                    "incomplete MoE shape: num_experts=%d num_experts_per_tok=%d moe_intermediate=%d (all must be > 0)",
+                    E, k, I);
+    if (k > E) return fail(MOE_ERR_INVALID_SHAPE, "num_experts_per_tok (%d) exceeds num_experts (%d)", k, E);
+    if (H <= 0 || H % kQ4Weights || I % kQ4Weights)
+        return fail(MOE_ERR_INVALID_SHAPE, "hidden_dim (%d) and moe_intermediate (%d) must be positive multiples of 256",
+                    H, I);
+    if (E > kMaxExperts || k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_SHAPE, "num_experts (%d) must be <= %d and num_experts_per_tok (%d) <= %d", E,
+                    kMaxExperts, k, kMaxTopK);
+    if ((long long)H * I > (1ll << 31) / 4 || (long long)E * H * I / 256 * 144 > (1ll << 40))
+        return fail(MOE_ERR_INVALID_SHAPE, "shape too large");
+    return MOE_OK;
+}
+
+size_t gate_bytes_of(const moe_ffn_shape &s) {
+    return (size_t)s.num_experts * s.moe_intermediate * (s.hidden_dim / kQ4Weights) * kQ4Bytes;
+}
+size_t down_bytes_of(const moe_ffn_shape &s) {
+    return (size_t)s.num_experts * s.hidden_dim * (s.moe_intermediate / kQ4Weights) * kQ4Bytes;
+}
+
+// Carve the workspace for cap tokens out of one allocation; returns its size.
+size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
+    const size_t T = cap, E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
+    const size_t S = T * k, nh = H / kQ4Weights, ni = I / kQ4Weights;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base ? base + off : nullptr;
+        off = align_up(off + bytes);
+        return p;
+    };
+    w->logits = (double *)take(T * E * 8);
+    w->idx = (int32_t *)take(S * 4);
+    w->w = (float *)take(S * 4);
+    w->rcount = (uint32_t *)take(T * 4);
+    w->counts = (int32_t *)take(E * 4);
+    w->offsets = (int32_t *)take((E + 1) * 4);
+    w->entries = (int32_t *)take(S * 4);
+    w->pos = (int32_t *)take(S * 4);
+    w->tiles = (int4 *)take((size_t)max_tiles((int)S, (int)E) * sizeof(int4));
+    w->n_tiles = (int32_t *)take(4);
+    w->x_hilo = (f16 *)take(T * 2 * H * 2);
+    w->x_xs = (f16 *)take(T * nh * 16 * 2);
+    w->x_sinv = (float *)take(T * nh * 4);
+    w->h = (float *)take(S * I * 4);
+    w->h_hilo = (f16 *)take(S * 2 * I * 2);
+    w->h_xs = (f16 *)take(S * ni * 16 * 2);
+    w->h_sinv = (float *)take(S * ni * 4);
+    w->Y = (float *)take(S * H * 4);
+    return off;
+}
+
+moe_status ensure_ws(moe_ffn_t h, int T, hipStream_t st) {
+    if (T <= h->cap) return MOE_OK;
+    Workspace w;
+    const size_t bytes = layout_ws(h->sh, T, nullptr, &w);
+    HIP_TRY(hipStreamSynchronize(st));
+    if (h->ws_base) {
+        HIP_TRY(hipFree(h->ws_base));
+        h->ws_base = nullptr;
+        h->cap = 0;
+    }
+    void *base = nullptr;
+    HIP_TRY(hipMalloc(&base, bytes));
+    layout_ws(h->sh, T, (char *)base, &w);
+    // router completion counters must start at zero; the kernel returns them to zero
+    hipError_t e = hipMemsetAsync(w.rcount, 0, (size_t)T * 4, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        (void)hipFree(base);
+        return fail(MOE_ERR_DEVICE, "workspace init failed: %s", hipGetErrorString(e));
+    }
+    h->ws_base = base;
+    h->ws = w;
+    h->cap = T;
+    return MOE_OK;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+template <int TT, int EV>
+void launch_router(moe_ffn_t h, int T, const float *x, int32_t *idx, float *w, hipStream_t st) {
+    const moe_ffn_shape &s = h->sh;
+    dim3 grid((T + TT - 1) / TT, (s.num_experts + 4 * EV - 1) / (4 * EV));
+    launch(h->prof, kStRouter, router_kernel<TT, EV>, grid, dim3(256), st, x, h->rw, h->rb, T, s.hidden_dim,
+           s.num_experts, s.num_experts_per_tok, h->ws.logits, idx, w, h->ws.rcount);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_ffn_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char *moe_ffn_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size_t gate_bytes, const void *up_q4k,
+                          size_t up_bytes, const void *down_q4k, size_t down_bytes, const float *router_w,
+                          const float *router_bias, void *stream, moe_ffn_t *out) {
+    g_err.clear();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_ffn_shape s = *shape;
+    const size_t gb = gate_bytes_of(s), db = down_bytes_of(s);
+    if (gate_bytes != gb || up_bytes != gb || down_bytes != db)
+        return fail(MOE_ERR_BLOB_SIZE, "blob sizes gate=%zu up=%zu down=%zu, shape needs gate=up=%zu down=%zu",
+                    gate_bytes, up_bytes, down_bytes, gb, db);
+    if (!gate_q4k || !up_q4k || !down_q4k || !router_w)
+        return fail(MOE_ERR_INVALID_ARG, "gate, up, down and router_w must not be NULL");
+    if (!is_device_ptr(gate_q4k) || !is_device_ptr(up_q4k) || !is_device_ptr(down_q4k) || !is_device_ptr(router_w) ||
+        (router_bias && !is_device_ptr(router_bias)))
+        return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
+    hipStream_t hs = (hipStream_t)stream;
+    moe_ffn_t h = new moe_ffn_s();
+    h->sh = s;
+    auto cleanup = [&](moe_status r) {
+        moe_ffn_destroy(h);
+        return r;
+    };
+    if (hipGetDevice(&h->device) != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "hipGetDevice failed"));
+    const int E = s.num_experts, H = s.hidden_dim, I = s.moe_intermediate;
+    if (hipMalloc(&h->gu, 2 * gb) != hipSuccess || hipMalloc(&h->dn, db) != hipSuccess ||
+        hipMalloc(&h->rw, (size_t)E * H * 4) != hipSuccess ||
+        (router_bias && hipMalloc(&h->rb, (size_t)E * 4) != hipSuccess))
+        return cleanup(fail(MOE_ERR_OOM, "weight allocation failed (%zu bytes)", 2 * gb + db));
+    hipError_t e = hipMemcpyAsync(h->rw, router_w, (size_t)E * H * 4, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess && router_bias) e = hipMemcpyAsync(h->rb, router_bias, (size_t)E * 4, hipMemcpyDeviceToDevice, hs);
+    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "router copy failed: %s", hipGetErrorString(e)));
+    const int nh = H / kQ4Weights, ni = I / kQ4Weights;
+    auto rep = [&](const void *src, uint8_t *dst, int rows, int nsb, int kind) {
+        const long total = (long)E * rows * nsb;
+        repack_kernel<<<(unsigned)((total + 255) / 256), 256, 0, hs>>>((const uint8_t *)src, dst, E, rows, nsb, kind);
+    };
+    rep(gate_q4k, h->gu, I, nh, 0);
+    rep(up_q4k, h->gu, I, nh, 1);
+    rep(down_q4k, h->dn, H, ni, 2);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "weight repack failed: %s", hipGetErrorString(e)));
+    *out = h;
+    return MOE_OK;
+}
+
+moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (max_tokens < 1) return fail(MOE_ERR_INVALID_SHAPE, "max_tokens must be >= 1 (got %d)", max_tokens);
+    return ensure_ws(h, max_tokens, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                           int32_t *router_idx, void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "token count must be >= 1 (got %d)", T);
+    const moe_ffn_shape &s = h->sh;
+    const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
+    if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x and out must not be NULL");
+    if (!is_device_ptr(x) || !is_device_ptr(out) || (router_out && !is_device_ptr(router_out)) ||
+        (router_idx && !is_device_ptr(router_idx)))
+        return fail(MOE_ERR_INVALID_ARG, "x, out, router_out, router_idx must be device pointers");
+    const size_t xb = (size_t)T * H * 4, kb = (size_t)T * k * 4;
+    if (overlaps(x, xb, out, xb)) return fail(MOE_ERR_INVALID_ARG, "out overlaps x");
+    if (router_out && (overlaps(router_out, kb, x, xb) || overlaps(router_out, kb, out, xb)))
+        return fail(MOE_ERR_INVALID_ARG, "router_out overlaps x or out");
+    if (router_idx && (overlaps(router_idx, kb, x, xb) || overlaps(router_idx, kb, out, xb) ||
+                       (router_out && overlaps(router_idx, kb, router_out, kb))))
+        return fail(MOE_ERR_INVALID_ARG, "router_idx overlaps another buffer");
+    hipStream_t st = (hipStream_t)stream;
+    moe_status r = ensure_ws(h, T, st);
+    if (r != MOE_OK) return r;
+    Workspace &w = h->ws;
+    int32_t *idx = router_idx ? router_idx : w.idx;
+    float *wt = router_out ? router_out : w.w;
+    const int S = T * k;
+    const int nh = H / kQ4Weights, ni = I / kQ4Weights;
+
+    Profiler &pf = h->prof;
+    if (T == 1)
+        launch_router<1, 1>(h, T, x, idx, wt, st);
+    else if (T <= 4)
+        launch_router<4, 1>(h, T, x, idx, wt, st);
+    else
+        launch_router<16, 4>(h, T, x, idx, wt, st);
+
+    launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,
+           w.tiles, w.n_tiles);
+
+    const long xunits = (long)T * nh;
+    launch(pf, kStStageX, stage_kernel, dim3((unsigned)((xunits + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
+           w.x_xs, w.x_sinv);
+
+    const int mt = max_tiles(S, E);
+    const int gu_groups = I / 8, dn_groups = H / kRowGroup;
+    launch(pf, kStGateUp, expert_m16_kernel<true>, dim3(mt, (gu_groups + 3) / 4), dim3(256), st, h->gu, gu_groups, nh,
+           w.tiles, w.n_tiles, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
+
+    const long hunits = (long)S * ni;
+    launch(pf, kStStageH, stage_kernel, dim3((unsigned)((hunits + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo,
+           w.h_xs, w.h_sinv);
+
+    launch(pf, kStDown, expert_m16_kernel<false>, dim3(mt, (dn_groups + 3) / 4), dim3(256), st, h->dn, dn_groups, ni,
+           w.tiles, w.n_tiles, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
+
+    launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
+
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+    h->last_T = T;
+    return MOE_OK;
+}
+
+moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets, int32_t *entries,
+                                 void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (h->last_T < 1) return fail(MOE_ERR_INVALID_ARG, "no forward has run on this handle");
+    if ((logits && !is_device_ptr(logits)) || (counts && !is_device_ptr(counts)) ||
+        (offsets && !is_device_ptr(offsets)) || (entries && !is_device_ptr(entries)))
+        return fail(MOE_ERR_INVALID_ARG, "debug outputs must be device pointers");
+    hipStream_t st = (hipStream_t)stream;
+    const size_t T = h->last_T, E = h->sh.num_experts, k = h->sh.num_experts_per_tok;
+    if (logits) HIP_TRY(hipMemcpyAsync(logits, h->ws.logits, T * E * 8, hipMemcpyDeviceToDevice, st));
+    if (counts) HIP_TRY(hipMemcpyAsync(counts, h->ws.counts, E * 4, hipMemcpyDeviceToDevice, st));
+    if (offsets) HIP_TRY(hipMemcpyAsync(offsets, h->ws.offsets, (E + 1) * 4, hipMemcpyDeviceToDevice, st));
+    if (entries) HIP_TRY(hipMemcpyAsync(entries, h->ws.entries, T * k * 4, hipMemcpyDeviceToDevice, st));
+    return MOE_OK;
+}
+
+moe_status moe_ffn_profile(moe_ffn_t h, uint32_t stage_mask) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    h->prof.mask = stage_mask & ((1u << kStCount) - 1u);
+    return MOE_OK;
+}
+
+moe_status moe_ffn_profile_read(moe_ffn_t h, double *ms, int32_t *launches) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!ms || !launches) return fail(MOE_ERR_INVALID_ARG, "ms and launches must not be NULL");
+    Profiler &p = h->prof;
+    for (int s = 0; s < kStCount; ++s) {
+        for (size_t i = 0; i < p.used[s]; ++i) {
+            HIP_TRY(hipEventSynchronize(p.pairs[s][i].second));
+            float e = 0.f;
+            HIP_TRY(hipEventElapsedTime(&e, p.pairs[s][i].first, p.pairs[s][i].second));
+            ms[s] += e;
+            launches[s] += 1;
+        }
+        p.used[s] = 0;
+    }
+    return MOE_OK;
+}
+
+int32_t moe_ffn_stage_count(void) { return kStCount; }
+
+const char *moe_ffn_stage_name(int32_t stage) { return (stage >= 0 && stage < kStCount) ? kStageNames[stage] : nullptr; }
+
+moe_status moe_ffn_destroy(moe_ffn_t h) {
+    if (!h) return MOE_OK;
+    (void)hipDeviceSynchronize();
+    if (h->gu) (void)hipFree(h->gu);
+    if (h->dn) (void)hipFree(h->dn);
+    if (h->rw) (void)hipFree(h->rw);
+    if (h->rb) (void)hipFree(h->rb);
+    if (h->ws_base) (void)hipFree(h->ws_base);
+    delete h;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,155 @@
+// Router: logits = W_r x (+ bias) in double, softmax over all experts, top-k,
+// renormalisation of the k weights.
+//
+// Defined by: forward_qwen3_moe_cuda_traced.rs (doc of
+// forward_qwen3_moe_cuda_traced_with_plan: the MoeRouter stage is a token's k
+// router weights after a softmax over the experts and a renormalisation over
+// the chosen k) and forward_qwen3_moe.rs step 2h (the chosen experts' outputs
+// are weighted by those router weights). Readings: the choice is made on the
+// logits (the softmax is monotone), larger first, equal logits to the lower
+// expert index; w_j = exp(l_j - l_max) / sum_i exp(l_i - l_max) over the
+// chosen i (the softmax denominator over all experts cancels).
+//
+// Grid: (token groups of TT tokens) x (expert groups of 4*EV experts); block
+// 256 = 4 waves, wave w owns experts w, w+4, ... of its group. Lanes split the
+// hidden dimension; products and sums are in double (fp32 inputs widen
+// exactly), so logits match an fp64 reference to ~1e-16 relative and the
+// top-k choice is exact except for true near-ties.
+// The last workgroup of a token group to finish (device-scope counter) runs
+// the softmax/top-k for that group's tokens, one wave per token.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kRouterChunk = 256;  // hidden columns staged per step
+
+template <int TT, int EV>
+__global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+                                                     const float *__restrict__ bias, int T, int H, int E, int k,
+                                                     double *__restrict__ logits, int32_t *__restrict__ idx_out,
+                                                     float *__restrict__ w_out, uint32_t *__restrict__ counters) {
+    __shared__ float xs[TT][kRouterChunk];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * TT;
+    const int nt = min(TT, T - t0);
+    const int e0 = blockIdx.y * 4 * EV;
+
+    double acc[EV][TT];
+#pragma unroll
+    for (int v = 0; v < EV; ++v)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) acc[v][t] = 0.0;
+
+    for (int h0 = 0; h0 < H; h0 += kRouterChunk) {
+        __syncthreads();
+        for (int i = tid; i < TT * kRouterChunk; i += 256) {
+            int t = i / kRouterChunk, c = i % kRouterChunk;
+            xs[t][c] = (t < nt) ? x[(size_t)(t0 + t) * H + h0 + c] : 0.f;
+        }
+        __syncthreads();
+        float4 xv[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xv[t] = *(const float4 *)&xs[t][lane * 4];
+#pragma unroll
+        for (int v = 0; v < EV; ++v) {
+            const int e = e0 + wave + 4 * v;
+            if (e < E) {
+                float4 wv = *(const float4 *)&wr[(size_t)e * H + h0 + lane * 4];
+                double w0 = wv.x, w1 = wv.y, w2 = wv.z, w3 = wv.w;
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    double a = acc[v][t];
+                    a = fma(w0, (double)xv[t].x, a);
+                    a = fma(w1, (double)xv[t].y, a);
+                    a = fma(w2, (double)xv[t].z, a);
+                    a = fma(w3, (double)xv[t].w, a);
+                    acc[v][t] = a;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < EV; ++v) {
+        const int e = e0 + wave + 4 * v;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            double s = wave_sum(acc[v][t]);
+            if (lane == 0 && e < E && t < nt) {
+                if (bias) s += (double)bias[e];
+                __hip_atomic_store(&logits[(size_t)(t0 + t) * E + e], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+
+    // Last workgroup of this token group does the selection.
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t prev = __hip_atomic_fetch_add(&counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == gridDim.y - 1);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+
+    for (int t = wave; t < nt; t += 4) {
+        const double *lrow = logits + (size_t)(t0 + t) * E;
+        const int per_lane = (E + 63) / 64;
+        double lv[kMaxExperts / 64];
+        uint32_t taken = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxExperts / 64; ++i) {
+            lv[i] = -INFINITY;
+            int e = lane + 64 * i;
+            if (i < per_lane && e < E) {
+                double v = __hip_atomic_load(&lrow[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                lv[i] = (v != v) ? -INFINITY : v;  // NaN never wins
+            } else {
+                taken |= 1u << i;
+            }
+        }
+        // Round j picks the largest untaken logit (lower index on ties); lane j
+        // keeps round j's winner. An untaken -inf still beats "nothing", so a
+        // valid expert is always chosen.
+        double my_v = -INFINITY, top_v = -INFINITY;
+        int my_i = 0;
+        for (int j = 0; j < k; ++j) {
+            double bv = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int i = 0; i < kMaxExperts / 64; ++i) {
+                int e = lane + 64 * i;
+                if (!((taken >> i) & 1) && (lv[i] > bv || (lv[i] == bv && e < bi))) {
+                    bv = lv[i];
+                    bi = e;
+                }
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                double ov = __shfl_xor(bv, o, kWave);
+                int oi = __shfl_xor(bi, o, kWave);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+            if (j == 0) top_v = bv;
+            if (lane == j) {
+                my_v = bv;
+                my_i = bi;
+            }
+        }
+        double ex = (lane < k) ? exp(my_v - top_v) : 0.0;
+        double z = wave_sum(ex);
+        if (lane < k) {
+            idx_out[(size_t)(t0 + t) * k + lane] = my_i;
+            w_out[(size_t)(t0 + t) * k + lane] = (float)(ex / z);
+        }
+    }
+    if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace moe
