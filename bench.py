@@ -1,0 +1,334 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE FFN layer (Q4_K experts) on one MI355X.
+
+One step = one call of the layer (router, bucketing, staging, gate/up with
+SwiGLU, down, combine) on one batch of T tokens already resident in HBM.
+The default workload is the Qwen3-30B-A3B-shaped decode layer (H=2048, E=128,
+k=8, I=768, T=1); the 2048-token Zipf-routed prefill of the same shape is
+measured beside it and reported under "prefill".
+
+Timing: W warmup steps, then K steps captured in one HIP graph and replayed
+between two events on the launch stream, with device synchronisation on both
+sides. Steps cycle over R replicas of the layer (distinct weights and inputs)
+whose weights total >= 1 GB, so the 256 MB Infinity Cache cannot hold the
+working set. The dominant kernel (gate_up) is then timed over K more eager
+steps with events stamped at its own start and end (hipExtLaunchKernelGGL);
+its roofline fraction uses algorithmic bytes (decode: routed gate+up Q4_K
+weight bytes) or flops (prefill: 2*T*k*2*H*I) per launch.
+
+The CPU baseline is the fp64 oracle as it stands, timed on this host on a
+bounded sample of the same workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-FFN tokens/s per layer + HBM GB/s (decode), MFMA TFLOP/s (prefill)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+REPLICA_BYTES = 1 << 30        # weights cycled per timed loop
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="30b-decode")
+    ap.add_argument("--prefill-workload", default="30b-prefill")
+    ap.add_argument("--prefill-steps", type=int, default=30)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--stages", action="store_true", help="also time every stage (eager pass, to stderr)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Bench:
+    """R replicas of one workload on the GPU, with their outputs preallocated."""
+
+    def __init__(self, wl, replicas: int, seed: int = 1):
+        import torch
+
+        import synth
+        from tests import parity
+
+        self.wl = wl
+        self.layers, self.xs, self.outs, self.ws, self.idxs = [], [], [], [], []
+        self.host0 = None
+        for r in range(replicas):
+            log(f"{wl.name}: generating replica {r + 1}/{replicas}")
+            inp = synth.make_inputs(wl, seed=seed, replica=r)
+            dev = parity.upload(inp)
+            layer, _ = parity.make_layer(inp, dev)
+            layer.reserve(wl.tokens)
+            x = dev["x"]
+            for key in ("gate", "up", "down", "router", "bias"):
+                dev[key] = None  # the layer owns its copies
+            if r == 0:
+                self.host0 = inp
+            self.layers.append(layer)
+            self.xs.append(x)
+            self.outs.append(torch.empty_like(x))
+            self.ws.append(torch.empty((wl.tokens, wl.top_k), dtype=torch.float32, device=x.device))
+            self.idxs.append(torch.empty((wl.tokens, wl.top_k), dtype=torch.int32, device=x.device))
+        torch.cuda.synchronize()
+
+    @property
+    def R(self):
+        return len(self.layers)
+
+    def step(self, i: int) -> None:
+        r = i % self.R
+        self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+
+    def routing(self):
+        """Per replica: distinct experts U, max tokens on one expert."""
+        import numpy as np
+        import torch
+
+        for r in range(self.R):
+            self.step(r)
+        torch.cuda.synchronize()
+        stats = []
+        for r in range(self.R):
+            idx = self.idxs[r].cpu().numpy()
+            cnt = np.bincount(idx.ravel(), minlength=self.wl.experts)
+            stats.append((int((cnt > 0).sum()), int(cnt.max())))
+        return stats
+
+    def timed(self, steps: int, warmup: int, eager: bool) -> float:
+        """Milliseconds per step."""
+        import torch
+
+        torch.cuda.synchronize()
+        if eager:
+            for i in range(warmup):
+                self.step(i)
+            torch.cuda.synchronize()
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            start.record()
+            for i in range(steps):
+                self.step(i)
+            end.record()
+            torch.cuda.synchronize()
+            return start.elapsed_time(end) / steps
+        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, capture_error_mode="relaxed"):
+            for i in range(max(warmup, 1)):
+                self.step(i)
+        with torch.cuda.graph(gt, capture_error_mode="relaxed"):
+            for i in range(steps):
+                self.step(i)
+        torch.cuda.synchronize()
+        gw.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        gt.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        del gw, gt
+        return ms
+
+    def stage_times(self, steps: int, stages) -> dict:
+        """{stage: [(replica, total ms, launches)]} from kernel-stamped events over `steps` eager steps."""
+        import torch
+
+        import quantized_moe_wave_amd as q
+
+        for layer in self.layers:
+            q.moe_ffn_profile(layer.handle, stages)
+        for i in range(steps):
+            self.step(i)
+        torch.cuda.synchronize()
+        res = {s: [] for s in stages}
+        for r, layer in enumerate(self.layers):
+            got = q.moe_ffn_profile_read(layer.handle)
+            q.moe_ffn_profile(layer.handle, [])
+            for s in stages:
+                res[s].append((r, got[s][0], got[s][1]))
+        return res
+
+    def close(self):
+        for layer in self.layers:
+            layer.close()
+        self.layers = []
+
+
+def replicas_for(wl) -> int:
+    layer_bytes = wl.experts * wl.expert_bytes + wl.experts * wl.hidden * 4
+    return max(1, math.ceil(REPLICA_BYTES / layer_bytes))
+
+
+def gate_up_bytes_per_expert(wl) -> int:
+    return 2 * wl.hidden * wl.inter * 144 // 256
+
+
+def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: bool):
+    b = Bench(wl, replicas_for(wl))
+    try:
+        stats = b.routing()
+        log(f"{wl.name}: routing per replica (distinct experts, max tokens/expert) = {stats}")
+        ms = b.timed(steps, warmup, eager)
+        log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'})")
+        prof = b.stage_times(steps, ["gate_up"])["gate_up"]
+        total_ms = sum(p[1] for p in prof)
+        launches = sum(p[2] for p in prof)
+        avg_us = total_ms / launches * 1e3
+        T, k, H, I = wl.tokens, wl.top_k, wl.hidden, wl.inter
+        if bound == "hbm":
+            # routed gate+up weight bytes of each launch, per replica
+            alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * n for r, _, n in prof)
+            achieved = alg / (total_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "expert_m16_kernel<true> (gate_up)", "avg_us": round(avg_us, 3)}
+        else:
+            flops = 2.0 * T * k * 2 * H * I
+            achieved = flops * launches / (total_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "expert_m16_kernel<true> (gate_up)", "avg_us": round(avg_us, 3)}
+        log(f"{wl.name}: gate_up avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")
+        if want_stages:
+            import quantized_moe_wave_amd as q
+
+            allp = b.stage_times(steps, q.moe_ffn_stage_names())
+            for s, lst in allp.items():
+                tm = sum(p[1] for p in lst)
+                n = sum(p[2] for p in lst)
+                log(f"{wl.name}: stage {s:8s} {tm / max(n, 1) * 1e3:9.2f} us avg over {n} launches")
+        U = sum(s[0] for s in stats) / len(stats)
+        return b, ms, stats, roof, U
+    except Exception:
+        b.close()
+        raise
+
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle on T=1 forwards of replica 0's weights, one token per call, for ~seconds."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    cores = oracle.set_threads(len(os.sched_getaffinity(0)))
+    wl = inp.wl
+    n, t0 = 0, time.perf_counter()
+    while True:
+        x = synth.gen_x(99, n, 1, wl.hidden)
+        oracle.forward(x, inp.router, inp.bias, inp.gate, inp.up, inp.down, wl.top_k)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and n >= 3:
+            break
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} single-token forwards of the {wl.name} layer (replica 0 weights), {el:.1f} s"}
+
+
+def copy_calibration(mb: int) -> None:
+    import torch
+
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.add(a, 0.0, out=b)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 5}))
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and timed on a single MI355X "
+              "(run with --gpus 1).", file=sys.stderr)
+        return 2
+    if args.copy_calibration_mb:
+        copy_calibration(args.copy_calibration_mb)
+        return 0
+    import torch
+
+    import synth
+
+    from quantized_moe_wave_amd.build import LIB
+
+    if not os.path.exists(LIB):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    wl = synth.WORKLOADS[args.workload]
+    b, ms, stats, roof, U = measure(wl, args.steps, args.warmup, args.eager, "hbm", args.stages)
+    host0 = b.host0
+    b.close()
+    del b
+    torch.cuda.empty_cache()
+    value = wl.tokens / (ms * 1e-3)
+    step_bytes = U * wl.expert_bytes
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
+                   "moe_intermediate": wl.inter, "tokens": wl.tokens, "replicas": replicas_for(wl),
+                   "timing": "eager" if args.eager else "hip-graph"},
+        "hbm_step": {"routed_expert_bytes": int(step_bytes), "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                     "unit": "GB/s", "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "distinct_experts": U},
+        "roofline": roof,
+    }
+    if not args.no_prefill:
+        pw = synth.WORKLOADS[args.prefill_workload]
+        pb, pms, pstats, proof, pU = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager,
+                                             "mfma", args.stages)
+        pb.close()
+        del pb
+        torch.cuda.empty_cache()
+        flops = 2.0 * pw.tokens * pw.top_k * 3 * pw.hidden * pw.inter + 2.0 * pw.tokens * pw.experts * pw.hidden
+        line["prefill"] = {
+            "workload": pw.name, "tokens": pw.tokens, "steps": args.prefill_steps, "ms_per_step": round(pms, 4),
+            "tokens_per_s": round(pw.tokens / (pms * 1e-3), 1),
+            "tflops": round(flops / (pms * 1e-3) / 1e12, 2),
+            "frac_mfma_peak": round(flops / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+            "distinct_experts": pU, "max_tokens_per_expert": max(s[1] for s in pstats), "roofline": proof,
+        }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {wl.name} for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(host0, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

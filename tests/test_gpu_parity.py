@@ -168,3 +168,33 @@ def test_error_returns():
     # the layer still works after the rejected calls
     g = parity.run_gpu(layer, x)
     parity.check_parity(inp, g)
+
+
+def test_graph_replay_matches_eager():
+    """The forward captured in a HIP graph, replayed several times with eager
+    work and synchronisations between replays: every replay equals eager."""
+    print("[parity] graph replay", flush=True)
+    import torch
+
+    inp, layer, dev = _layer("30b-batch")
+    x = dev["x"]
+    eager = parity.run_gpu(layer, x)
+    layer.reserve(x.shape[0])
+    out = torch.empty_like(x)
+    w = torch.empty((x.shape[0], layer.top_k), dtype=torch.float32, device=x.device)
+    idx = torch.empty((x.shape[0], layer.top_k), dtype=torch.int32, device=x.device)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        layer.forward(x, out, w, idx)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        w.zero_()
+        idx.fill_(-1)
+        other = parity.run_gpu(layer, x[: 5 + rep])  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.out.view(np.uint32)), rep
+        assert np.array_equal(w.cpu().numpy(), eager.w) and np.array_equal(idx.cpu().numpy(), eager.idx), rep
+        assert other.out.shape[0] == 5 + rep
