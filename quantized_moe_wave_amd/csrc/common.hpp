@@ -41,6 +41,27 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ f16x2 u32_as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t f16x2_as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
+// Cross-workgroup hand-off without cache maintenance. Data handed to another
+// workgroup of the same launch is written with agent-scope atomic stores and
+// read with agent-scope atomic loads (coherent accesses on this multi-XCD
+// part), so no L2 writeback/invalidate (what a device-wide fence costs) is
+// needed: the writer only waits until its stores have completed before it
+// bumps the completion counter.
+__device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ uint32_t counter_arrive(uint32_t *c) {
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// LDS writes of this wave visible to its other lanes: wait for LDS operations
+// only (s_waitcnt lgkmcnt(0); vmcnt and expcnt left at their maxima so global
+// loads and stores stay in flight), then keep the compiler from moving LDS
+// accesses across the point.
+__device__ __forceinline__ void lds_wave_sync() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -22,6 +22,7 @@
 #include "../../include/moe_ffn.h"
 #include "bucket.hpp"
 #include "common.hpp"
+#include "decode.hpp"
 #include "expert.hpp"
 #include "repack.hpp"
 #include "router.hpp"
@@ -336,6 +337,20 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
     Profiler &pf = h->prof;
+    const int mt = max_tiles(S, E);
+    if (T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6) {
+        // decode path: three launches (see decode.hpp)
+        launch(pf, kStRouter, router_small_kernel, dim3((E + 3) / 4), dim3(256), st, x, h->rw, h->rb, T, H, E, k,
+               w.logits, w.x_hilo, w.x_xs, w.x_sinv, w.rcount, idx, wt, w.counts, w.offsets, w.entries, w.pos);
+        launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(256), st, h->gu, I / 8, nh, idx, k, w.x_hilo,
+               w.x_xs, w.x_sinv, w.h, I);
+        launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup, T), dim3(kDcWaves * 64), st, h->dn,
+               H / kRowGroup, ni, idx, wt, k, w.h, I, out, H);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
+        h->last_T = T;
+        return MOE_OK;
+    }
     if (T == 1)
         launch_router<1, 1>(h, T, x, idx, wt, st);
     else if (T <= 4)
@@ -350,7 +365,6 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     launch(pf, kStStageX, stage_kernel, dim3((unsigned)((xunits + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
            w.x_xs, w.x_sinv);
 
-    const int mt = max_tiles(S, E);
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
     launch(pf, kStGateUp, expert_m16_kernel<true>, dim3(mt, (gu_groups + 3) / 4), dim3(256), st, h->gu, gu_groups, nh,
            w.tiles, w.n_tiles, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv, w.h, I);

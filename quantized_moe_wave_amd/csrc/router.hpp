@@ -24,6 +24,162 @@ namespace moe {
 
 constexpr int kRouterChunk = 256;  // hidden columns staged per step
 
+constexpr int kRankMaxExperts = 256;  // rank-based selection up to this many experts
+
+// One wave: top-k of one token's E <= kRankMaxExperts logits by rank. Each
+// candidate c counts the logits that beat it (larger, or equal with a lower
+// index); the k candidates with rank < k are the chosen experts and rank is
+// their slot. Same result as k rounds of argmax with the lower-index rule, in
+// fp64, without a serial chain of cross-lane steps. lds: this wave's scratch
+// of kRankMaxExperts + kMaxTopK doubles + kMaxTopK ints.
+template <int PL>
+__device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
+                                               int *sidx, double *lds) {
+    const int lane = threadIdx.x & 63;
+    double v[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        const double x = __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v[i] = (c < E && x == x) ? x : -INFINITY;  // NaN never wins
+        lds[c] = v[i];                              // entries >= E pad with -inf
+    }
+    lds_wave_sync();
+    int rank[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) rank[i] = 0;
+    // 16 logits per step, read as 8 broadcast 16-byte LDS loads issued together
+    for (int j0 = 0; j0 < 64 * PL; j0 += 16) {
+        double a[16];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const double2 p2 = *(const double2 *)&lds[j0 + 2 * q];
+            a[2 * q] = p2.x;
+            a[2 * q + 1] = p2.y;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int j = j0 + q;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) {
+                const int c = lane + 64 * i;
+                rank[i] += (int)(a[q] > v[i]) | ((int)(a[q] == v[i]) & (int)(j < c));  // branch-free
+            }
+        }
+    }
+    // winners into LDS (value and expert at their slot), global stores last
+    double *sel = lds + kRankMaxExperts;
+    int *sel_i = (int *)(sel + kMaxTopK);
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        if (c < E && rank[i] < k) {
+            sel[rank[i]] = v[i];
+            sel_i[rank[i]] = c;
+        }
+    }
+    lds_wave_sync();
+    const double ex = (lane < k) ? exp(sel[lane] - sel[0]) : 0.0;
+    const double z = wave_sum(ex);
+    if (lane < k) {
+        const int c = sel_i[lane];
+        idx_row[lane] = c;
+        w_row[lane] = (float)(ex / z);
+        if (sidx) sidx[lane] = c;
+    }
+    lds_wave_sync();
+}
+
+// Top-k of one token on one wave; dispatches on the expert count.
+__device__ __forceinline__ void topk_any_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
+                                              int *sidx, double *lds);
+
+// One wave: top-k of one token's E logits (device memory written by other
+// workgroups of this launch, read with agent-scope loads) and the renormalised
+// weights. Lane j < k writes slot j; sidx (optional, LDS) receives the experts.
+__device__ __forceinline__ void topk_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
+                                          int *sidx) {
+    const int lane = threadIdx.x & 63;
+    const int per_lane = (E + 63) / 64;
+    double lv[kMaxExperts / 64];
+    uint32_t taken = 0;
+    // loads of a uniform number of chunks, clamped to a valid expert, so they
+    // are all in flight together
+    for (int i0 = 0; i0 < kMaxExperts / 64; i0 += 4) {
+        if (i0 >= per_lane) break;
+        double v4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v4[i] = __hip_atomic_load(&lrow[min(lane + 64 * (i0 + i), E - 1)], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * (i0 + i);
+            lv[i0 + i] = (e < E && v4[i] == v4[i]) ? v4[i] : -INFINITY;  // NaN never wins
+            if (e >= E) taken |= 1u << (i0 + i);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxExperts / 64; ++i) {
+        if (i >= ((per_lane + 3) & ~3)) {
+            lv[i] = -INFINITY;
+            taken |= 1u << i;
+        }
+    }
+    // Round j picks the largest untaken logit (lower index on ties); lane j
+    // keeps round j's winner. An untaken -inf still beats "nothing", so a
+    // valid expert is always chosen.
+    double my_v = -INFINITY, top_v = -INFINITY;
+    int my_i = 0;
+    for (int j = 0; j < k; ++j) {
+        double bv = -INFINITY;
+        int bi = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < kMaxExperts / 64; ++i) {
+            int e = lane + 64 * i;
+            if (!((taken >> i) & 1) && (lv[i] > bv || (lv[i] == bv && e < bi))) {
+                bv = lv[i];
+                bi = e;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            double ov = __shfl_xor(bv, o, kWave);
+            int oi = __shfl_xor(bi, o, kWave);
+            if (ov > bv || (ov == bv && oi < bi)) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+        if (j == 0) top_v = bv;
+        if (lane == j) {
+            my_v = bv;
+            my_i = bi;
+        }
+    }
+    double ex = (lane < k) ? exp(my_v - top_v) : 0.0;
+    double z = wave_sum(ex);
+    if (lane < k) {
+        idx_row[lane] = my_i;
+        w_row[lane] = (float)(ex / z);
+        if (sidx) sidx[lane] = my_i;
+    }
+}
+
+
+__device__ __forceinline__ void topk_any_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
+                                              int *sidx, double *lds) {
+    if (E <= 64)
+        topk_rank_wave<1>(lrow, E, k, idx_row, w_row, sidx, lds);
+    else if (E <= 128)
+        topk_rank_wave<2>(lrow, E, k, idx_row, w_row, sidx, lds);
+    else if (E <= kRankMaxExperts)
+        topk_rank_wave<4>(lrow, E, k, idx_row, w_row, sidx, lds);
+    else
+        topk_wave(lrow, E, k, idx_row, w_row, sidx);
+}
+
 template <int TT, int EV>
 __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x, const float *__restrict__ wr,
                                                      const float *__restrict__ bias, int T, int H, int E, int k,
@@ -84,71 +240,16 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
     }
 
     // Last workgroup of this token group does the selection.
-    __threadfence();
+    wait_own_stores();
     __syncthreads();
-    if (tid == 0) {
-        uint32_t prev = __hip_atomic_fetch_add(&counters[blockIdx.x], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == gridDim.y - 1);
-    }
+    if (tid == 0) s_last = (counter_arrive(&counters[blockIdx.x]) == gridDim.y - 1);
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
-    for (int t = wave; t < nt; t += 4) {
-        const double *lrow = logits + (size_t)(t0 + t) * E;
-        const int per_lane = (E + 63) / 64;
-        double lv[kMaxExperts / 64];
-        uint32_t taken = 0;
-#pragma unroll
-        for (int i = 0; i < kMaxExperts / 64; ++i) {
-            lv[i] = -INFINITY;
-            int e = lane + 64 * i;
-            if (i < per_lane && e < E) {
-                double v = __hip_atomic_load(&lrow[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                lv[i] = (v != v) ? -INFINITY : v;  // NaN never wins
-            } else {
-                taken |= 1u << i;
-            }
-        }
-        // Round j picks the largest untaken logit (lower index on ties); lane j
-        // keeps round j's winner. An untaken -inf still beats "nothing", so a
-        // valid expert is always chosen.
-        double my_v = -INFINITY, top_v = -INFINITY;
-        int my_i = 0;
-        for (int j = 0; j < k; ++j) {
-            double bv = -INFINITY;
-            int bi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < kMaxExperts / 64; ++i) {
-                int e = lane + 64 * i;
-                if (!((taken >> i) & 1) && (lv[i] > bv || (lv[i] == bv && e < bi))) {
-                    bv = lv[i];
-                    bi = e;
-                }
-            }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                double ov = __shfl_xor(bv, o, kWave);
-                int oi = __shfl_xor(bi, o, kWave);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-            if (j == 0) top_v = bv;
-            if (lane == j) {
-                my_v = bv;
-                my_i = bi;
-            }
-        }
-        double ex = (lane < k) ? exp(my_v - top_v) : 0.0;
-        double z = wave_sum(ex);
-        if (lane < k) {
-            idx_out[(size_t)(t0 + t) * k + lane] = my_i;
-            w_out[(size_t)(t0 + t) * k + lane] = (float)(ex / z);
-        }
-    }
+    __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
+    for (int t = wave; t < nt; t += 4)
+        topk_any_wave(logits + (size_t)(t0 + t) * E, E, k, idx_out + (size_t)(t0 + t) * k,
+                      w_out + (size_t)(t0 + t) * k, nullptr, tk_lds[wave]);
     if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

@@ -198,3 +198,32 @@ def test_graph_replay_matches_eager():
         assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.out.view(np.uint32)), rep
         assert np.array_equal(w.cpu().numpy(), eager.w) and np.array_equal(idx.cpu().numpy(), eager.idx), rep
         assert other.out.shape[0] == 5 + rep
+
+
+def test_exact_ties_many_experts():
+    """x = 0 makes all 128 logits equal: the lower-index rule picks 0..k-1."""
+    print("[parity] 30b ties", flush=True)
+    inp, layer, _ = _layer("30b-batch")
+    for T in (1, 3, 9):
+        x = np.zeros((T, inp.wl.hidden), np.float32)
+        inp2, g = _run(inp, layer, x)
+        assert np.array_equal(g.idx, np.tile(np.arange(8), (T, 1)))
+        assert np.all(g.w == np.float32(0.125)) and np.all(g.out == 0.0)
+        parity.check_parity(inp2, g)
+
+
+@pytest.mark.parametrize("T", [3, 20])
+def test_many_experts(T):
+    """E = 300 > 256 takes the iterated-argmax selection; k = 6."""
+    print(f"[parity] E=300 k=6 T={T}", flush=True)
+    import dataclasses
+
+    import synth as _s
+
+    wl = dataclasses.replace(_s.WORKLOADS["tiny"], name="e300", experts=300, top_k=6)
+    key = ("e300", T)
+    inp = _s.make_inputs(wl, seed=21)
+    layer, dev = parity.make_layer(inp)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=31 + T))
+    parity.check_parity(inp2, g)
+    layer.close()
