@@ -101,7 +101,7 @@ class Bench:
         self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
 
     def routing(self):
-        """Per replica: distinct experts U, max tokens on one expert."""
+        """Per replica: (distinct experts U, max tokens on one expert, rows in full 128-row tiles)."""
         import numpy as np
         import torch
 
@@ -112,7 +112,7 @@ class Bench:
         for r in range(self.R):
             idx = self.idxs[r].cpu().numpy()
             cnt = np.bincount(idx.ravel(), minlength=self.wl.experts)
-            stats.append((int((cnt > 0).sum()), int(cnt.max())))
+            stats.append((int((cnt > 0).sum()), int(cnt.max()), int((cnt // 128 * 128).sum())))
         return stats
 
     def timed(self, steps: int, warmup: int, eager: bool) -> float:
@@ -191,25 +191,31 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
         log(f"{wl.name}: routing per replica (distinct experts, max tokens/expert) = {stats}")
         ms = b.timed(steps, warmup, eager)
         log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'})")
-        prof = b.stage_times(steps, ["gate_up"])["gate_up"]
-        total_ms = sum(p[1] for p in prof)
-        launches = sum(p[2] for p in prof)
-        avg_us = total_ms / launches * 1e3
         T, k, H, I = wl.tokens, wl.top_k, wl.hidden, wl.inter
         if bound == "hbm":
-            # routed gate+up weight bytes of each launch, per replica
-            alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * n for r, _, n in prof)
+            # decode: the gate/up kernel; routed gate+up weight bytes of each launch
+            stage = "gate_up"
+            prof = b.stage_times(steps, [stage])[stage]
+            total_ms = sum(p[1] for p in prof)
+            launches = sum(p[2] for p in prof)
+            alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * nl for r, _, nl in prof)
             achieved = alg / (total_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "expert_m16_kernel<true> (gate_up)", "avg_us": round(avg_us, 3)}
+                    "kernel": "gateup_pair_kernel (gate_up)", "avg_us": round(total_ms / launches * 1e3, 3)}
         else:
-            flops = 2.0 * T * k * 2 * H * I
-            achieved = flops * launches / (total_ms * 1e-3) / 1e12
+            # prefill: the 128-row-tile gate/up GEMM; 2 * rows * 2I * H flops per launch
+            stage = "gate_up_big"
+            prof = b.stage_times(steps, [stage])[stage]
+            total_ms = sum(p[1] for p in prof)
+            launches = sum(p[2] for p in prof)
+            flops = sum(2.0 * stats[r][2] * 2 * I * H * nl for r, _, nl in prof)
+            achieved = flops / (total_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "expert_m16_kernel<true> (gate_up)", "avg_us": round(avg_us, 3)}
-        log(f"{wl.name}: gate_up avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")
+                    "kernel": "expert_gemm_kernel<true> (gate_up_big)", "avg_us": round(total_ms / launches * 1e3, 3)}
+        avg_us = total_ms / launches * 1e3
+        log(f"{wl.name}: {stage} avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")
         if want_stages:
             import quantized_moe_wave_amd as q
 
@@ -218,7 +224,7 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
                 tm = sum(p[1] for p in lst)
                 n = sum(p[2] for p in lst)
                 log(f"{wl.name}: stage {s:8s} {tm / max(n, 1) * 1e3:9.2f} us avg over {n} launches")
-        U = sum(s[0] for s in stats) / len(stats)
+        U = sum(st[0] for st in stats) / len(stats)
         return b, ms, stats, roof, U
     except Exception:
         b.close()
@@ -321,7 +327,8 @@ def main() -> int:
             "tokens_per_s": round(pw.tokens / (pms * 1e-3), 1),
             "tflops": round(flops / (pms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(flops / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "distinct_experts": pU, "max_tokens_per_expert": max(s[1] for s in pstats), "roofline": proof,
+            "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
+            "rows_in_128_tiles": sum(st[2] for st in pstats) / len(pstats), "roofline": proof,
         }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {wl.name} for ~{args.cpu_seconds:.0f} s")

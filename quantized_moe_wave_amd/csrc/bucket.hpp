@@ -9,8 +9,10 @@
 //
 // Layout (bit-exact, deterministic): counts[e]; offsets[e] = sum of counts
 // below e, offsets[E] = T*k; entries[offsets[e] + r] = t*k + j for the r-th
-// pair in token order that chose e. Tiles of up to kTileM consecutive entries
-// of one expert: tiles[i] = (e, first entry, rows); n_tiles = their number.
+// pair in token order that chose e. Each expert's entries are cut into full
+// tiles of kBigTileM rows (big_tiles, for the grouped GEMM) followed by tiles
+// of up to kTileM rows for the rest (tiles); entries (e, first entry, rows).
+// n_tiles[0] = number of small tiles, n_tiles[1] = number of big tiles.
 //
 // Grid: E workgroups (one per expert), 256 threads. Every workgroup builds the
 // full histogram in LDS (integer atomics only), so no workgroup waits for
@@ -20,13 +22,16 @@
 
 namespace moe {
 
+constexpr int kBigTileM = 128;
+
 __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
                                                      int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                      int32_t *__restrict__ entries, int32_t *__restrict__ pos,
-                                                     int4 *__restrict__ tiles, int32_t *__restrict__ n_tiles) {
+                                                     int4 *__restrict__ tiles, int4 *__restrict__ big_tiles,
+                                                     int32_t *__restrict__ n_tiles) {
     __shared__ int cnt[kMaxExperts];
-    __shared__ int red[2][4];
-    __shared__ int wave_tot[4];
+    __shared__ int red[3][4];
+    __shared__ int wave_tot[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x;
     const int S = T * k;
@@ -37,39 +42,53 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
     __syncthreads();
 
     // Entries and tiles below expert e.
-    int below = 0, tiles_below = 0, tiles_all = 0;
+    int below = 0, tiles_below = 0, big_below = 0, tiles_all = 0, big_all = 0;
     for (int i = tid; i < E; i += 256) {
-        int c = cnt[i];
-        int nt = (c + kTileM - 1) / kTileM;
-        tiles_all += nt;
+        const int c = cnt[i];
+        const int nb = c / kBigTileM;
+        const int ns = (c - nb * kBigTileM + kTileM - 1) / kTileM;
+        tiles_all += ns;
+        big_all += nb;
         if (i < e) {
             below += c;
-            tiles_below += nt;
+            tiles_below += ns;
+            big_below += nb;
         }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         below += __shfl_xor(below, o, kWave);
         tiles_below += __shfl_xor(tiles_below, o, kWave);
+        big_below += __shfl_xor(big_below, o, kWave);
         tiles_all += __shfl_xor(tiles_all, o, kWave);
+        big_all += __shfl_xor(big_all, o, kWave);
     }
     if (lane == 0) {
         red[0][wave] = below;
         red[1][wave] = tiles_below;
-        wave_tot[wave] = tiles_all;
+        red[2][wave] = big_below;
+        wave_tot[0][wave] = tiles_all;
+        wave_tot[1][wave] = big_all;
     }
     __syncthreads();
     const int off = red[0][0] + red[0][1] + red[0][2] + red[0][3];
     const int toff = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    const int boff = red[2][0] + red[2][1] + red[2][2] + red[2][3];
     const int mine = cnt[e];
+    const int nbig = mine / kBigTileM;
+    const int rem = mine - nbig * kBigTileM;
     if (tid == 0) {
         counts[e] = mine;
         offsets[e] = off;
         if (e == E - 1) offsets[E] = off + mine;
-        if (e == 0) *n_tiles = wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+        if (e == 0) {
+            n_tiles[0] = wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
+            n_tiles[1] = wave_tot[1][0] + wave_tot[1][1] + wave_tot[1][2] + wave_tot[1][3];
+        }
     }
-    for (int i = tid; i * kTileM < mine; i += 256)
-        tiles[toff + i] = make_int4(e, off + i * kTileM, min(kTileM, mine - i * kTileM), 0);
+    for (int i = tid; i < nbig; i += 256) big_tiles[boff + i] = make_int4(e, off + i * kBigTileM, kBigTileM, 0);
+    for (int i = tid; i * kTileM < rem; i += 256)
+        tiles[toff + i] = make_int4(e, off + nbig * kBigTileM + i * kTileM, min(kTileM, rem - i * kTileM), 0);
     if (mine == 0) return;
 
     // Stable scatter: tokens in ascending order, 256 per pass.
@@ -85,16 +104,16 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
         const uint64_t ball = __ballot(flag);
         const int rank_in_wave = __popcll(ball & ((1ull << lane) - 1ull));
         __syncthreads();
-        if (lane == 0) wave_tot[wave] = __popcll(ball);
+        if (lane == 0) wave_tot[0][wave] = __popcll(ball);
         __syncthreads();
         int before = 0;
-        for (int w = 0; w < wave; ++w) before += wave_tot[w];
+        for (int w = 0; w < wave; ++w) before += wave_tot[0][w];
         if (flag) {
             const int p = base + before + rank_in_wave;
             entries[p] = t * k + j;
             pos[(size_t)t * k + j] = p;
         }
-        base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+        base += wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
     }
 }
 

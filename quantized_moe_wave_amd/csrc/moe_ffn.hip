@@ -24,6 +24,7 @@
 #include "common.hpp"
 #include "decode.hpp"
 #include "expert.hpp"
+#include "gemm.hpp"
 #include "repack.hpp"
 #include "router.hpp"
 #include "stage.hpp"
@@ -65,8 +66,9 @@ struct Workspace {
     int32_t *offsets = nullptr;   // [E+1]
     int32_t *entries = nullptr;   // [S]
     int32_t *pos = nullptr;       // [S]
-    int4 *tiles = nullptr;        // [max tiles]
-    int32_t *n_tiles = nullptr;   // [1]
+    int4 *tiles = nullptr;        // [max tiles] 16-row tiles
+    int4 *big_tiles = nullptr;    // [S/128] 128-row tiles
+    int32_t *n_tiles = nullptr;   // [2] small, big
     f16 *x_hilo = nullptr;        // [T][2H]
     f16 *x_xs = nullptr;          // [T][H/256][16]
     float *x_sinv = nullptr;      // [T][H/256]
@@ -79,8 +81,20 @@ struct Workspace {
 
 int max_tiles(int S, int E) { return S / kTileM + std::min(E, S); }
 
-enum Stage { kStRouter = 0, kStBucket, kStStageX, kStGateUp, kStStageH, kStDown, kStCombine, kStCount };
-const char *const kStageNames[kStCount] = {"router", "bucket", "stage_x", "gate_up", "stage_h", "down", "combine"};
+enum Stage {
+    kStRouter = 0,
+    kStBucket,
+    kStStageX,
+    kStGateUp,
+    kStGateUpBig,
+    kStStageH,
+    kStDown,
+    kStDownBig,
+    kStCombine,
+    kStCount
+};
+const char *const kStageNames[kStCount] = {"router",  "bucket", "stage_x",  "gate_up", "gate_up_big",
+                                           "stage_h", "down",   "down_big", "combine"};
 
 // Start/stop events of profiled stages. A profiled kernel is launched with
 // hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
@@ -110,6 +124,19 @@ struct Profiler {
             }
     }
 };
+
+// Launch kernel on st with dynamic LDS; if stage s is profiled, bracket it
+// with its events.
+template <typename... KArgs, typename... Args>
+void launch_lds(Profiler &pf, int s, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                Args... args) {
+    auto ev = pf.next(s);
+    if (ev.first)
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, ev.first, ev.second, 0,
+                              static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, lds, st>>>(static_cast<KArgs>(args)...);
+}
 
 // Launch kernel on st; if stage s is profiled, bracket it with its events.
 template <typename... KArgs, typename... Args>
@@ -194,7 +221,8 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
     w->entries = (int32_t *)take(S * 4);
     w->pos = (int32_t *)take(S * 4);
     w->tiles = (int4 *)take((size_t)max_tiles((int)S, (int)E) * sizeof(int4));
-    w->n_tiles = (int32_t *)take(4);
+    w->big_tiles = (int4 *)take((S / kBigTileM + 1) * sizeof(int4));
+    w->n_tiles = (int32_t *)take(8);
     w->x_hilo = (f16 *)take(T * 2 * H * 2);
     w->x_xs = (f16 *)take(T * nh * 16 * 2);
     w->x_sinv = (float *)take(T * nh * 4);
@@ -272,6 +300,14 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
         (router_bias && !is_device_ptr(router_bias)))
         return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
     hipStream_t hs = (hipStream_t)stream;
+    {
+        hipError_t a1 = hipFuncSetAttribute((const void *)expert_gemm_kernel<true>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+        hipError_t a2 = hipFuncSetAttribute((const void *)expert_gemm_kernel<false>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+        if (a1 != hipSuccess || a2 != hipSuccess)
+            return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernel's LDS limit to %zu bytes", kGemmLds);
+    }
     moe_ffn_t h = new moe_ffn_s();
     h->sh = s;
     auto cleanup = [&](moe_status r) {
@@ -359,15 +395,20 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         launch_router<16, 4>(h, T, x, idx, wt, st);
 
     launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,
-           w.tiles, w.n_tiles);
+           w.tiles, w.big_tiles, w.n_tiles);
 
     const long xunits = (long)T * nh;
     launch(pf, kStStageX, stage_kernel, dim3((unsigned)((xunits + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
            w.x_xs, w.x_sinv);
 
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
+    const int nbig = S / kBigTileM;
     launch(pf, kStGateUp, expert_m16_kernel<true>, dim3(mt, (gu_groups + 3) / 4), dim3(256), st, h->gu, gu_groups, nh,
            w.tiles, w.n_tiles, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
+    if (nbig > 0)
+        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true>, dim3(nbig, gu_groups / kBigGroups), dim3(256), kGemmLds,
+                   st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
+                   w.h, I);
 
     const long hunits = (long)S * ni;
     launch(pf, kStStageH, stage_kernel, dim3((unsigned)((hunits + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo,
@@ -375,6 +416,10 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
 
     launch(pf, kStDown, expert_m16_kernel<false>, dim3(mt, (dn_groups + 3) / 4), dim3(256), st, h->dn, dn_groups, ni,
            w.tiles, w.n_tiles, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
+    if (nbig > 0)
+        launch_lds(pf, kStDownBig, expert_gemm_kernel<false>, dim3(nbig, dn_groups / kBigGroups), dim3(256), kGemmLds,
+                   st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv,
+                   w.Y, H);
 
     launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
 

@@ -227,3 +227,18 @@ def test_many_experts(T):
     inp2, g = _run(inp, layer, _x(inp, T, seed=31 + T))
     parity.check_parity(inp2, g)
     layer.close()
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 300), ("30b-batch", 300)])
+def test_big_tiles_full_parity(name, T):
+    """A bias that sends every token to expert 0 makes 128-row grouped-GEMM
+    tiles (plus a remainder) that the oracle can check element by element;
+    the 30b shape also has an odd super-block count on the down projection."""
+    print(f"[parity] big tiles {name} T={T}", flush=True)
+    E = synth.WORKLOADS[name].experts
+    bias = np.zeros(E, np.float32)
+    bias[0] = 40.0
+    inp, layer, _ = _layer(name, seed=8, bias=bias)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=77))
+    assert g.counts[0] == T
+    parity.check_parity(inp2, g)
