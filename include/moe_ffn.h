@@ -110,7 +110,8 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
  * Asynchronous on stream: nothing waits on the host, except that a T above
  * the reserved capacity first grows the workspace (a device synchronisation).
  * Non-finite inputs give unspecified routing and outputs.
- * Errors: INVALID_SHAPE (T < 1), INVALID_ARG (null/host pointers, out
+ * Errors: INVALID_SHAPE (T < 1, or T so large that T*2*hidden_dim or
+ * T*k*2*moe_intermediate reaches 2^32), INVALID_ARG (null/host pointers, out
  * overlapping x, bad handle), OOM, DEVICE. */
 moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                            int32_t *router_idx, void *stream);
@@ -127,9 +128,10 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
                                  int32_t *entries, void *stream);
 
 /* Per-stage GPU timing for benchmarks. Stages of one forward, in launch order:
- * 0 router, 1 bucket, 2 stage_x, 3 gate_up (16-row tiles, or the per-pair
- * decode kernel), 4 gate_up_big (128-row tiles), 5 stage_h, 6 down (16-row
- * tiles, or the fused decode down + combine), 7 down_big, 8 combine; a stage a
+ * 0 router, 1 bucket, 2 stage_x, 3 gate_up (16-row tiles of buckets of at
+ * most 16 entries, or the per-pair decode kernel), 4 gate_up_big (GEMM tiles of
+ * up to 64 rows for larger buckets), 5 stage_h, 6 down (16-row tiles, or the
+ * fused decode down + combine), 7 down_big (GEMM tiles), 8 combine; a stage a
  * forward does not run has no launches (moe_ffn_stage_name gives the name,
  * moe_ffn_stage_count the number).
  * moe_ffn_profile sets a bit mask of stages; while it is non-zero, each forward

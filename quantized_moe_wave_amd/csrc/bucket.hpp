@@ -9,20 +9,24 @@
 //
 // Layout (bit-exact, deterministic): counts[e]; offsets[e] = sum of counts
 // below e, offsets[E] = T*k; entries[offsets[e] + r] = t*k + j for the r-th
-// pair in token order that chose e. Each expert's entries are cut into full
-// tiles of kBigTileM rows (big_tiles, for the grouped GEMM) followed by tiles
-// of up to kTileM rows for the rest (tiles); entries (e, first entry, rows).
-// n_tiles[0] = number of small tiles, n_tiles[1] = number of big tiles.
+// pair in token order that chose e. A bucket of at least kGemmMinRows entries
+// is cut into tiles of up to kGemmM rows for the grouped GEMM (big_tiles);
+// a smaller one into tiles of up to kTileM rows (tiles). Tile records are
+// (e, first entry, rows, 0), in expert order. n_tiles[0] = number of small
+// tiles, n_tiles[1] = number of GEMM tiles.
 //
 // Grid: E workgroups (one per expert), 256 threads. Every workgroup builds the
 // full histogram in LDS (integer atomics only), so no workgroup waits for
 // another.
 #pragma once
 #include "common.hpp"
+#include "gemm.hpp"
 
 namespace moe {
 
-constexpr int kBigTileM = 128;
+// GEMM tiles and 16-row tiles of a bucket of c entries.
+__device__ __forceinline__ int gemm_tiles_of(int c) { return c >= kGemmMinRows ? (c + kGemmM - 1) / kGemmM : 0; }
+__device__ __forceinline__ int small_tiles_of(int c) { return c >= kGemmMinRows ? 0 : (c + kTileM - 1) / kTileM; }
 
 __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
                                                      int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -45,8 +49,8 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
     int below = 0, tiles_below = 0, big_below = 0, tiles_all = 0, big_all = 0;
     for (int i = tid; i < E; i += 256) {
         const int c = cnt[i];
-        const int nb = c / kBigTileM;
-        const int ns = (c - nb * kBigTileM + kTileM - 1) / kTileM;
+        const int nb = gemm_tiles_of(c);
+        const int ns = small_tiles_of(c);
         tiles_all += ns;
         big_all += nb;
         if (i < e) {
@@ -75,8 +79,8 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
     const int toff = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     const int boff = red[2][0] + red[2][1] + red[2][2] + red[2][3];
     const int mine = cnt[e];
-    const int nbig = mine / kBigTileM;
-    const int rem = mine - nbig * kBigTileM;
+    const int nbig = gemm_tiles_of(mine);
+    const int nsmall = small_tiles_of(mine);
     if (tid == 0) {
         counts[e] = mine;
         offsets[e] = off;
@@ -86,9 +90,10 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
             n_tiles[1] = wave_tot[1][0] + wave_tot[1][1] + wave_tot[1][2] + wave_tot[1][3];
         }
     }
-    for (int i = tid; i < nbig; i += 256) big_tiles[boff + i] = make_int4(e, off + i * kBigTileM, kBigTileM, 0);
-    for (int i = tid; i * kTileM < rem; i += 256)
-        tiles[toff + i] = make_int4(e, off + nbig * kBigTileM + i * kTileM, min(kTileM, rem - i * kTileM), 0);
+    for (int i = tid; i < nbig; i += 256)
+        big_tiles[boff + i] = make_int4(e, off + i * kGemmM, min(kGemmM, mine - i * kGemmM), 0);
+    for (int i = tid; i < nsmall; i += 256)
+        tiles[toff + i] = make_int4(e, off + i * kTileM, min(kTileM, mine - i * kTileM), 0);
     if (mine == 0) return;
 
     // Stable scatter: tokens in ascending order, 256 per pass.

@@ -1,4 +1,5 @@
-// Expert matmuls with fused Q4_K dequantisation on gfx950 MFMA.
+// Q4_K-on-MFMA building blocks shared by the expert kernels (gemm.hpp,
+// decode.hpp), and the combine kernel.
 //
 // The pages' expert step (forward_qwen3_moe.rs module doc and step 2h): each
 // chosen expert dequantises its Q4_K gate/up/down bytes inside its matvecs,
@@ -14,10 +15,6 @@
 // v_mfma_f32_16x16x16_f16 per super-block with A = the 8 staged 32-column
 // sums (hi | lo) and B = the 8 mins (exact). The epilogue of each super-block
 // adds sinv * (d * P - dmin * Q) to the running fp32 result.
-//
-// Tile: 16 tokens (rows of A, one expert bucket tile) x 16 weight rows (one
-// repacked row group) per wave; 4 waves per workgroup take 4 consecutive row
-// groups of the same tile. Every wave walks the whole reduction dimension.
 //
 // MFMA register layouts used (16x16 tiles, 64 lanes, lane l):
 //   A: row l%16, k-slot group l/16;  B: column l%16, same k-slot group;
@@ -51,6 +48,65 @@ __device__ __forceinline__ f16x8 q_times_scale(uint32_t dA, uint32_t dB, int nib
     return out;
 }
 
+// Both k-steps held by the same 8 bytes dA, dB: the low nibbles (k-step with
+// scale sc_lo) and the high nibbles (scale sc_hi), as exact fp16 sc * q in the
+// element order of q_times_scale. A low nibble or-ed into fp16 1024.0 (0x6400)
+// reads as 1024 + q; a high nibble left in place (bits 4-7) and or-ed into fp16
+// 64.0 (0x5400) reads as 64 + q, since one mantissa unit of 64.0 is 1/16. One
+// fma per pair then removes the offset and applies the scale, exactly.
+// Masks and magic halves for q_times_scale_pair, held in VGPRs: with two
+// literal operands (v_and_or_b32 takes at most one, and no two SGPRs) the
+// compiler would split each and-or into two instructions.
+struct NibbleConsts {
+    uint32_t lo_mask, hi_mask, lo_magic, hi_magic;
+};
+__device__ __forceinline__ NibbleConsts nibble_consts() {
+    NibbleConsts c;
+    uint32_t a = 0x000F000Fu, b = 0x00F000F0u, m = 0x64006400u, h = 0x54005400u;
+    asm volatile("" : "+v"(a), "+v"(b), "+v"(m), "+v"(h));
+    c.lo_mask = a;
+    c.hi_mask = b;
+    c.lo_magic = m;
+    c.hi_magic = h;
+    return c;
+}
+
+__device__ __forceinline__ void q_times_scale_pair(uint32_t dA, uint32_t dB, f16 sc_lo, f16 sc_hi, f16x8 &blo,
+                                                   f16x8 &bhi, const NibbleConsts &k) {
+    const uint32_t a8 = dA >> 8, b8 = dB >> 8;
+    const f16x2 s0 = {sc_lo, sc_lo}, n0 = s0 * (f16)(-1024.f);
+    const f16x2 s1 = {sc_hi, sc_hi}, n1 = s1 * (f16)(-64.f);
+    const f16x2 l0 = __builtin_elementwise_fma(u32_as_f16x2((dA & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 0, 2
+    const f16x2 l1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 1, 3
+    const f16x2 l2 = __builtin_elementwise_fma(u32_as_f16x2((dB & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 4, 6
+    const f16x2 l3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 5, 7
+    const f16x2 h0 = __builtin_elementwise_fma(u32_as_f16x2((dA & k.hi_mask) | k.hi_magic), s1, n1);
+    const f16x2 h1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & k.hi_mask) | k.hi_magic), s1, n1);
+    const f16x2 h2 = __builtin_elementwise_fma(u32_as_f16x2((dB & k.hi_mask) | k.hi_magic), s1, n1);
+    const f16x2 h3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & k.hi_mask) | k.hi_magic), s1, n1);
+    blo[0] = l0[0]; blo[1] = l0[1]; blo[2] = l1[0]; blo[3] = l1[1];
+    blo[4] = l2[0]; blo[5] = l2[1]; blo[6] = l3[0]; blo[7] = l3[1];
+    bhi[0] = h0[0]; bhi[1] = h0[1]; bhi[2] = h1[0]; bhi[3] = h1[1];
+    bhi[4] = h2[0]; bhi[5] = h2[1]; bhi[6] = h3[0]; bhi[7] = h3[1];
+}
+
+// One k-step of the 8 bytes dA, dB (NIB 0: low nibbles, 1: high), as in
+// q_times_scale_pair.
+template <int NIB>
+__device__ __forceinline__ f16x8 q_times_scale_nib(uint32_t dA, uint32_t dB, f16 sc, const NibbleConsts &k) {
+    const uint32_t a8 = dA >> 8, b8 = dB >> 8;
+    const uint32_t mask = NIB ? k.hi_mask : k.lo_mask, magic = NIB ? k.hi_magic : k.lo_magic;
+    const f16x2 s2 = {sc, sc}, n2 = s2 * (f16)(NIB ? -64.f : -1024.f);
+    const f16x2 r0 = __builtin_elementwise_fma(u32_as_f16x2((dA & mask) | magic), s2, n2);  // bytes 0, 2
+    const f16x2 r1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & mask) | magic), s2, n2);  // bytes 1, 3
+    const f16x2 r2 = __builtin_elementwise_fma(u32_as_f16x2((dB & mask) | magic), s2, n2);  // bytes 4, 6
+    const f16x2 r3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & mask) | magic), s2, n2);  // bytes 5, 7
+    f16x8 out;
+    out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
+    out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
+    return out;
+}
+
 // The 8 six-bit scales (sc) and mins (mn) of a header, one byte each.
 __device__ __forceinline__ void unpack_scales(u32x4 hdr, uint32_t sc[2], uint32_t mn[2]) {
     const uint32_t s0 = hdr.y, s1 = hdr.z, s2 = hdr.w;  // scale bytes 0-3, 4-7, 8-11
@@ -62,105 +118,6 @@ __device__ __forceinline__ void unpack_scales(u32x4 hdr, uint32_t sc[2], uint32_
 
 __device__ __forceinline__ uint32_t byte_of(const uint32_t w[2], int j) { return (w[j >> 2] >> (8 * (j & 3))) & 0xFFu; }
 
-// GATEUP: W = repacked gate/up matrix (I/8 row groups, K = H); A rows are the
-//   tokens of the tile's bucket entries; output h[slot][I] = SiLU(g) * u.
-// !GATEUP: W = repacked down matrix (H/16 row groups, K = I); A rows are the
-//   tile's slots; output Y[slot][H].
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void expert_m16_kernel(const uint8_t *__restrict__ W, int ngroups, int nsb,
-                                                         const int4 *__restrict__ tiles,
-                                                         const int32_t *__restrict__ n_tiles,
-                                                         const int32_t *__restrict__ entries, int k,
-                                                         const f16 *__restrict__ a_hilo,
-                                                         const f16 *__restrict__ a_xs,
-                                                         const float *__restrict__ a_sinv,
-                                                         float *__restrict__ outp, int out_ld) {
-    const int tile = blockIdx.x;
-    if (tile >= *n_tiles) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int rg = blockIdx.y * 4 + wave;
-    if (rg >= ngroups) return;
-    const int4 ti = tiles[tile];
-    const int e = ti.x, r0 = ti.y, rows = ti.z;
-    const int n = lane & 15, g = lane >> 4;
-    const int K = nsb * kQ4Weights;
-
-    // A row of this lane, and the 4 output rows it accumulates.
-    const bool a_ok = n < rows;
-    const int a_row = a_ok ? (GATEUP ? entries[r0 + n] / k : r0 + n) : 0;
-    int o_row[4];
-    bool o_ok[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        o_ok[i] = m < rows;
-        o_row[i] = o_ok[i] ? (GATEUP ? entries[r0 + m] / k : r0 + m) : 0;
-    }
-
-    const uint8_t *wg = W + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
-    const f16 *arow = a_hilo + (size_t)a_row * (2 * K) + g * 16;
-
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < nsb; ++b) {
-        const uint8_t *blk = wg + (size_t)b * kGroupSbBytes;
-        const u32x4 q0 = *(const u32x4 *)(blk + lane * 16);
-        const u32x4 q1 = *(const u32x4 *)(blk + 1024 + lane * 16);
-        const u32x4 hdr = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
-        uint32_t sc[2], mn[2];
-        unpack_scales(hdr, sc, mn);
-        const float d = half_bits_to_float(hdr.x & 0xFFFFu);
-        const float dmin = half_bits_to_float(hdr.x >> 16);
-
-        f32x4 P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const u32x4 &q = (s < 4) ? q0 : q1;
-            const int cc = (s >> 1) & 1;   // chunk within the half
-            const int nib = s & 1;         // low / high nibble
-            const uint32_t dA = cc ? q.z : q.x;
-            const uint32_t dB = cc ? q.w : q.y;
-            const f16 scv = (f16)(float)byte_of(sc, s);
-            const f16x2 sc2 = {scv, scv};
-            const f16x2 neg2 = sc2 * (f16)(-1024.f);
-            const f16x8 B = q_times_scale(dA, dB, nib, sc2, neg2);
-            f16x8 Ahi = {}, Alo = {};
-            if (a_ok) {
-                const f16 *ap = arow + (size_t)(b * 8 + s) * 64;
-                Ahi = *(const f16x8 *)ap;
-                Alo = *(const f16x8 *)(ap + 8);
-            }
-            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, B, P, 0, 0, 0);
-            P = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, B, P, 0, 0, 0);
-        }
-        // min term: A' = 4 of the 8 sub-block sums (hi for g < 2, lo for g >= 2),
-        // B' = the matching 4 mins.
-        f16x4 Am = {};
-        if (a_ok) Am = *(const f16x4 *)(a_xs + ((size_t)a_row * nsb + b) * 16 + 4 * g);
-        f16x4 Bm;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) Bm[i] = (f16)(float)byte_of(mn, 4 * (g & 1) + i);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 Q = __builtin_amdgcn_mfma_f32_16x16x16f16(Am, Bm, zero, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float sv = o_ok[i] ? a_sinv[(size_t)o_row[i] * nsb + b] : 0.f;
-            acc[i] += sv * (d * P[i] - dmin * Q[i]);
-        }
-    }
-
-    if (GATEUP) {
-        // lanes n < 8 hold gate row 8rg+n, lanes n+8 the matching up row
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float u = __shfl_xor(acc[i], 8, kWave);
-            if (n < 8 && o_ok[i]) outp[(size_t)(r0 + 4 * g + i) * out_ld + rg * 8 + n] = silu_f(acc[i]) * u;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (o_ok[i]) outp[(size_t)(r0 + 4 * g + i) * out_ld + rg * kRowGroup + n] = acc[i];
-    }
-}
 
 // out[t][:] = sum_{j=0..k-1} w[t][j] * Y[pos[t*k+j]][:], slot 0 first (fixed
 // order, no atomics). Grid (ceil(H/1024), T), 256 threads x 4 columns.

@@ -67,7 +67,7 @@ struct Workspace {
     int32_t *entries = nullptr;   // [S]
     int32_t *pos = nullptr;       // [S]
     int4 *tiles = nullptr;        // [max tiles] 16-row tiles
-    int4 *big_tiles = nullptr;    // [S/128] 128-row tiles
+    int4 *big_tiles = nullptr;    // [max_gemm_tiles] GEMM tiles (up to 64 rows)
     int32_t *n_tiles = nullptr;   // [2] small, big
     f16 *x_hilo = nullptr;        // [T][2H]
     f16 *x_xs = nullptr;          // [T][H/256][16]
@@ -79,7 +79,10 @@ struct Workspace {
     float *Y = nullptr;           // [S][H]
 };
 
-int max_tiles(int S, int E) { return S / kTileM + std::min(E, S); }
+// 16-row tiles: only buckets of fewer than kGemmMinRows (<= 16) entries take
+// them, one tile each.
+int max_tiles(int S, int E) { return max_small_tiles(S, E); }
+static_assert(kGemmMinRows <= kTileM + 1, "a small bucket must fit one 16-row tile");
 
 enum Stage {
     kStRouter = 0,
@@ -221,7 +224,7 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
     w->entries = (int32_t *)take(S * 4);
     w->pos = (int32_t *)take(S * 4);
     w->tiles = (int4 *)take((size_t)max_tiles((int)S, (int)E) * sizeof(int4));
-    w->big_tiles = (int4 *)take((S / kBigTileM + 1) * sizeof(int4));
+    w->big_tiles = (int4 *)take((size_t)max_gemm_tiles((int)S, (int)E) * sizeof(int4));
     w->n_tiles = (int32_t *)take(8);
     w->x_hilo = (f16 *)take(T * 2 * H * 2);
     w->x_xs = (f16 *)take(T * nh * 16 * 2);
@@ -301,12 +304,19 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
         return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
     hipStream_t hs = (hipStream_t)stream;
     {
-        hipError_t a1 = hipFuncSetAttribute((const void *)expert_gemm_kernel<true>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        hipError_t a2 = hipFuncSetAttribute((const void *)expert_gemm_kernel<false>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-        if (a1 != hipSuccess || a2 != hipSuccess)
-            return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernel's LDS limit to %zu bytes", kGemmLds);
+        const hipError_t a[4] = {
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)GemmShape<4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)GemmShape<4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)GemmShape<1>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)GemmShape<1>::Lds)};
+        for (hipError_t e : a)
+            if (e != hipSuccess)
+                return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
+                            GemmShape<4>::Lds, hipGetErrorString(e));
     }
     moe_ffn_t h = new moe_ffn_s();
     h->sh = s;
@@ -352,6 +362,10 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "token count must be >= 1 (got %d)", T);
     const moe_ffn_shape &s = h->sh;
     const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
+    // staged rows are addressed with 32-bit half offsets
+    if ((uint64_t)T * 2 * H >= (1ull << 32) || (uint64_t)T * k * 2 * I >= (1ull << 32))
+        return fail(MOE_ERR_INVALID_SHAPE, "token count %d too large for this layer (T*2*H and T*k*2*I must be < 2^32)",
+                    T);
     if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x and out must not be NULL");
     if (!is_device_ptr(x) || !is_device_ptr(out) || (router_out && !is_device_ptr(router_out)) ||
         (router_idx && !is_device_ptr(router_idx)))
@@ -373,7 +387,6 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
     Profiler &pf = h->prof;
-    const int mt = max_tiles(S, E);
     if (T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6) {
         // decode path: three launches (see decode.hpp)
         launch(pf, kStRouter, router_small_kernel, dim3((E + 3) / 4), dim3(256), st, x, h->rw, h->rb, T, H, E, k,
@@ -401,25 +414,30 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     launch(pf, kStStageX, stage_kernel, dim3((unsigned)((xunits + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
            w.x_xs, w.x_sinv);
 
+    // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
+    // (see gemm.hpp); 16-row tiles for buckets of at most 16 entries, 64-row
+    // tiles for larger ones.
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
-    const int nbig = S / kBigTileM;
-    launch(pf, kStGateUp, expert_m16_kernel<true>, dim3(mt, (gu_groups + 3) / 4), dim3(256), st, h->gu, gu_groups, nh,
-           w.tiles, w.n_tiles, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
-    if (nbig > 0)
-        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true>, dim3(nbig, gu_groups / kBigGroups), dim3(256), kGemmLds,
-                   st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
-                   w.h, I);
+    const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
+    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1>, dim3(8 * (gu_groups / kGemmGroups) * ms8), dim3(256),
+               GemmShape<1>::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo, w.x_xs,
+               w.x_sinv, w.h, I);
+    if (S >= kGemmMinRows)
+        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4>, dim3(8 * (gu_groups / kGemmGroups) * mg8),
+                   dim3(256), GemmShape<4>::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
+                   w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
 
     const long hunits = (long)S * ni;
     launch(pf, kStStageH, stage_kernel, dim3((unsigned)((hunits + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo,
            w.h_xs, w.h_sinv);
 
-    launch(pf, kStDown, expert_m16_kernel<false>, dim3(mt, (dn_groups + 3) / 4), dim3(256), st, h->dn, dn_groups, ni,
-           w.tiles, w.n_tiles, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
-    if (nbig > 0)
-        launch_lds(pf, kStDownBig, expert_gemm_kernel<false>, dim3(nbig, dn_groups / kBigGroups), dim3(256), kGemmLds,
-                   st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv,
-                   w.Y, H);
+    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1>, dim3(8 * (dn_groups / kGemmGroups) * ms8), dim3(256),
+               GemmShape<1>::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo, w.h_xs,
+               w.h_sinv, w.Y, H);
+    if (S >= kGemmMinRows)
+        launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4>, dim3(8 * (dn_groups / kGemmGroups) * mg8),
+                   dim3(256), GemmShape<4>::Lds, st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k,
+                   w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
 
     launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
 
