@@ -128,12 +128,12 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
                                  int32_t *entries, void *stream);
 
 /* Per-stage GPU timing for benchmarks. Stages of one forward, in launch order:
- * 0 router, 1 bucket, 2 stage_x, 3 gate_up (16-row tiles of buckets of at
- * most 16 entries, or the per-pair decode kernel), 4 gate_up_big (GEMM tiles of
- * up to 64 rows for larger buckets), 5 stage_h, 6 down (16-row tiles, or the
- * fused decode down + combine), 7 down_big (GEMM tiles), 8 combine; a stage a
- * forward does not run has no launches (moe_ffn_stage_name gives the name,
- * moe_ffn_stage_count the number).
+ * 0 router (logits, and for at most 4 tokens also the top-k), 1 topk, 2 bucket,
+ * 3 stage_x, 4 gate_up (16-row tiles of buckets of at most 16 entries, or the
+ * per-pair decode kernel), 5 gate_up_big (tiles of up to 64 rows for larger
+ * buckets), 6 stage_h, 7 down (16-row tiles, or the fused decode down +
+ * combine), 8 down_big, 9 combine; a stage a forward does not run has no
+ * launches (moe_ffn_stage_name gives the name, moe_ffn_stage_count the number).
  * moe_ffn_profile sets a bit mask of stages; while it is non-zero, each forward
  * records a HIP event on its stream right before and right after every
  * selected stage's kernel. moe_ffn_profile_read waits for those events, adds

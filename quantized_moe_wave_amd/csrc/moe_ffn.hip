@@ -2,7 +2,8 @@
 // repack, workspace, and the per-call launch sequence.
 //
 // forward(T) enqueues, all on the caller's stream, with no host wait:
-//   1. router_kernel   logits (fp64), top-k, renormalised weights
+//   1. router_kernel   logits (fp64), top-k, renormalised weights (a few
+//                      tokens), or router_logits_kernel + topk_kernel
 //   2. bucket_kernel   stable counting sort of (token, slot) by expert + tiles
 //   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums
 //   4. expert GATEUP   gate/up Q4_K MFMA + SiLU(g)*u -> h[slot][I]
@@ -86,6 +87,7 @@ static_assert(kGemmMinRows <= kTileM + 1, "a small bucket must fit one 16-row ti
 
 enum Stage {
     kStRouter = 0,
+    kStTopk,
     kStBucket,
     kStStageX,
     kStGateUp,
@@ -96,8 +98,8 @@ enum Stage {
     kStCombine,
     kStCount
 };
-const char *const kStageNames[kStCount] = {"router",  "bucket", "stage_x",  "gate_up", "gate_up_big",
-                                           "stage_h", "down",   "down_big", "combine"};
+const char *const kStageNames[kStCount] = {"router",      "topk",    "bucket", "stage_x",  "gate_up",
+                                           "gate_up_big", "stage_h", "down",   "down_big", "combine"};
 
 // Start/stop events of profiled stages. A profiled kernel is launched with
 // hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
@@ -400,12 +402,15 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         h->last_T = T;
         return MOE_OK;
     }
-    if (T == 1)
+    if (T == 1) {
         launch_router<1, 1>(h, T, x, idx, wt, st);
-    else if (T <= 4)
+    } else if (T <= 4) {
         launch_router<4, 1>(h, T, x, idx, wt, st);
-    else
-        launch_router<16, 4>(h, T, x, idx, wt, st);
+    } else {
+        launch(pf, kStRouter, router_logits_kernel, dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp),
+               dim3(256), st, x, h->rw, h->rb, T, H, E, w.logits);
+        launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
+    }
 
     launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,
            w.tiles, w.big_tiles, w.n_tiles);

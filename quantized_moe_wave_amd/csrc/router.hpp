@@ -253,4 +253,116 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
     if (tid == 0) __hip_atomic_store(&counters[blockIdx.x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens: logits on fp64 MFMA, then top-k in a second launch.
+//
+// v_mfma_f64_16x16x4_f64 takes fp64 operands and accumulates in fp64; the
+// fp32 inputs widen exactly and their products are exact, so the logits are
+// an fp64 sum of exact products (as in the plain definition) up to summation
+// order.
+//
+// Workgroup tile: 32 tokens x 32 experts, 4 waves; wave w sums the hidden
+// columns [w*H/4, (w+1)*H/4) into 2 x 2 MFMA tiles (16 tokens x 16 experts
+// each), and the 4 partial tiles are added in wave order through LDS (a fixed
+// order: results are reproducible).
+// Column pairing: for 16 consecutive columns from k0, lane l (n = l%16,
+// g = l/16) loads the 4 floats at k0 + 4g of its token row (A) and of its
+// expert row (B); MFMA step i (0..3) uses element i, so lane group g covers
+// column k0 + 4g + i in step i on both sides and every column is used once.
+// MFMA layouts (64 lanes): A lane l = A[row l%16][k l/16], B lane l =
+// B[k l/16][col l%16], D lane l element r = D[row l/16 + 4r][col l%16] (the
+// fp64 shape interleaves rows unlike the fp32 16x16 shapes).
+constexpr int kRlTok = 32, kRlExp = 32, kRlPf = 4;  // tile, and 16-column groups loaded ahead
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+                                                            const float *__restrict__ bias, int T, int H, int E,
+                                                            double *__restrict__ logits) {
+    __shared__ double part[4][2][2][4][64];  // [wave][token block][expert block][element][lane]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int t0 = blockIdx.x * kRlTok, e0 = blockIdx.y * kRlExp;
+    const int kq = H >> 2;                  // columns per wave (a multiple of 64)
+    const int kbeg = wave * kq;
+    const int ngrp = kq >> 4;               // 16-column groups per wave
+
+    // rows of this lane (clamped: rows past T or E load a valid row, never stored)
+    const float *xr[2], *wrow[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        xr[b] = x + (size_t)min(t0 + 16 * b + n, T - 1) * H + kbeg + 4 * g;
+        wrow[b] = wr + (size_t)min(e0 + 16 * b + n, E - 1) * H + kbeg + 4 * g;
+    }
+
+    f64x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+
+    // register ring of kRlPf groups: group j sits in slot j % kRlPf
+    float4 ra[kRlPf][2], rb[kRlPf][2];
+    auto load_grp = [&](int j, float4 (&a)[2], float4 (&b)[2]) {
+        const int jj = min(j, ngrp - 1);  // past the end: reload the last group (unused)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            a[t] = *(const float4 *)(xr[t] + 16 * jj);
+            b[t] = *(const float4 *)(wrow[t] + 16 * jj);
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < kRlPf; ++j) load_grp(j, ra[j], rb[j]);
+
+    for (int j0 = 0; j0 < ngrp; j0 += kRlPf) {
+#pragma unroll
+        for (int u = 0; u < kRlPf; ++u) {
+            const float4 a0 = ra[u][0], a1 = ra[u][1], b0 = rb[u][0], b1 = rb[u][1];
+            load_grp(j0 + u + kRlPf, ra[u], rb[u]);
+            const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
+            const float bv[2][4] = {{b0.x, b0.y, b0.z, b0.w}, {b1.x, b1.y, b1.z, b1.w}};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                    for (int eb = 0; eb < 2; ++eb)
+                        acc[tb][eb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[tb][i], (double)bv[eb][i],
+                                                                          acc[tb][eb], 0, 0, 0);
+        }
+    }
+
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[wave][tb][eb][r][lane] = acc[tb][eb][r];
+    __syncthreads();
+    // 1024 outputs, 4 per thread: combo c = (tb, eb, r, lane)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = threadIdx.x + 256 * q;
+        const int l = c & 63, r = (c >> 6) & 3, eb = (c >> 8) & 1, tb = c >> 9;
+        const int t = t0 + 16 * tb + (l >> 4) + 4 * r, e = e0 + 16 * eb + (l & 15);
+        double v = part[0][tb][eb][r][l];
+        v += part[1][tb][eb][r][l];
+        v += part[2][tb][eb][r][l];
+        v += part[3][tb][eb][r][l];
+        if (t < T && e < E) logits[(size_t)t * E + e] = bias ? v + (double)bias[e] : v;
+    }
+}
+
+// Top-k and renormalised weights of 4 tokens per workgroup, one wave each,
+// from logits written by the previous launch.
+__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, int T, int E, int k,
+                                                   int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
+    const int wave = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    topk_any_wave(logits + (size_t)t * E, E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr,
+                  tk_lds[wave]);
+}
+
 }  // namespace moe
