@@ -1,17 +1,19 @@
 // Small-batch (decode) path: T <= kSmallT tokens per call, three launches.
 //
-//   router_small_kernel       router logits (fp64) and x staging; the last
-//                             workgroup to finish (device-scope counter) does
-//                             the top-k, renormalisation and bucket layout of
-//                             all T tokens
+//   router_small_kernel       router logits (fp64) and x staging
 //   gateup_pair_kernel        one (token, slot) pair x one 16-row weight group
 //                             per workgroup, the four waves splitting the
-//                             reduction dimension
+//                             reduction dimension; the workgroup finds the
+//                             pair's expert itself (top-k of its token)
 //   down_combine_small_kernel down projection of one token's k experts fused
-//                             with the router-weighted sum (slot order)
+//                             with the router-weighted sum (slot order), again
+//                             with its own top-k; one extra workgroup writes
+//                             the routing outputs (indices, weights, bucket
+//                             layout)
 //
-// The hand-off to the last workgroup moves only the fp64 logits, through
-// agent-scope atomic stores/loads (no cache maintenance).
+// Every workgroup recomputing its token's top-k from the logits (a few
+// hundred fp64 compares per thread) is cheaper at decode than handing the
+// choice between workgroups, which costs several dependent memory round trips.
 //
 // Same arithmetic as the general path (router.hpp, stage.hpp, expert.hpp); the
 // layer's definition and the readings are cited there. Only the work split
@@ -114,75 +116,69 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
     }
 }
 
-// Rank-based top-k of one token for a whole workgroup (E <= 256 = one
-// candidate per thread): the k winners' experts and logits land in LDS at
-// their slot. Same rule as the other selections: larger logit first, equal
-// logits to the lower index; NaN counts as -inf.
+// Rank-based top-k of one token for a whole workgroup (E <= 256): the k
+// winners' experts and logits land in LDS at their slot. Same rule as the
+// other selections: larger logit first, equal logits to the lower index; NaN
+// counts as -inf. The logits are padded with -inf to 256 entries (a pad never
+// beats a real candidate: it is not larger, and on a tie its index is higher).
+// Candidate c's rank counts the logits that beat it, in fp64. Every lane of a
+// wave walks the same range of j, so each LDS read is a broadcast: for
+// E <= 128 candidate c = tid % 128 and waves 0-1 count j < 64, waves 2-3
+// j >= 64; for larger E candidate c = tid counts all 256.
 template <bool COHERENT>
 __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, double *lg, int *sel_e,
                                            double *sel_v) {
-    __shared__ float lgf[kRankMaxExperts];
+    __shared__ int rk_hi[128];
     const int tid = threadIdx.x;
-    for (int c = tid; c < E; c += 256) {
+    const bool act = tid < 256;  // threads past 256 (larger workgroups) only join the barriers
+    if (act) {
         // COHERENT: written by other workgroups of this launch (agent-scope load)
+        const int c = min(tid, E - 1);
         const double v = COHERENT ? __hip_atomic_load(&lrow[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lrow[c];
-        const double vv = (v == v) ? v : -INFINITY;
-        lg[c] = vv;
-        lgf[c] = (float)vv;  // rounding is monotone: lgf[j] > lgf[c] implies lg[j] > lg[c]
+        lg[tid] = (tid < E && v == v) ? v : -INFINITY;
     }
     __syncthreads();
-    // E <= 128: two threads per candidate, each counting half of the logits;
-    // E <= 256: one thread per candidate. The count runs on the fp32 copies;
-    // where fp32 copies are equal (only then can they disagree with fp64) the
-    // pair is decided in fp64 with the lower-index rule, so the ranks are
-    // exactly the fp64 ranks.
-    const int half = (E <= 128) ? 2 : 1;
-    const int c = (half == 2) ? (tid >> 1) : tid;
-    const int jb = (half == 2) ? (tid & 1) * ((E + 1) / 2) : 0;
-    const int je = (half == 2) ? min(E, jb + (E + 1) / 2) : E;
-    const bool live = c < E;
-    const double v = live ? lg[c] : -INFINITY;
-    const float vf = live ? lgf[c] : -INFINITY;
+    const bool split = E <= 128;
+    const int c = split ? (tid & 127) : (tid & 255);
+    const int j0 = split ? ((tid >> 7) & 1) * 64 : 0;
+    const int nj = act ? (split ? 64 : 256) : 0;
+    const double v = lg[c];
     int rank = 0;
-    for (int j0 = jb; j0 < je; j0 += 16) {
-        float a[16];
+    for (int jj = 0; jj < nj; jj += 8) {
+        double b[8];
 #pragma unroll
-        for (int q = 0; q < 16; ++q) a[q] = lgf[min(j0 + q, E - 1)];
-        uint32_t tie = 0;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const bool in = live && (j0 + q < je);
-            rank += (int)(in & (a[q] > vf));
-            tie |= (uint32_t)(in & (a[q] == vf) & (j0 + q != c)) << q;
+        for (int q = 0; q < 4; ++q) {
+            const double2 p2 = *(const double2 *)&lg[j0 + jj + 2 * q];
+            b[2 * q] = p2.x;
+            b[2 * q + 1] = p2.y;
         }
-        if (__ballot(tie != 0)) {  // rare: settle equal fp32 copies in fp64
 #pragma unroll
-            for (int q = 0; q < 16; ++q) {
-                if ((tie >> q) & 1) {
-                    const double b = lg[j0 + q];
-                    rank += (int)(b > v) | ((int)(b == v) & (int)(j0 + q < c));
-                }
-            }
+        for (int q = 0; q < 8; ++q) {
+            const int j = j0 + jj + q;
+            rank += (int)(b[q] > v) | ((int)(b[q] == v) & (int)(j < c));  // branch-free
         }
     }
-    if (half == 2) rank += __shfl_xor(rank, 1, kWave);
-    if (live && (half == 1 || (tid & 1) == 0) && rank < k) {
-        sel_e[rank] = c;
-        sel_v[rank] = v;
+    if (act && split && tid >= 128) rk_hi[c] = rank;
+    __syncthreads();
+    if (act && c < E && (!split || tid < 128)) {
+        if (split) rank += rk_hi[c];
+        if (rank < k) {
+            sel_e[rank] = c;
+            sel_v[rank] = v;
+        }
     }
     __syncthreads();
 }
 
 // Routing outputs of all T tokens: idx/w per token, then the stable bucket
-// layout of the T*k <= 256 pairs.
+// layout of the T*k <= 256 pairs, the latter by wave 0 alone (lane l owns
+// experts 4l .. 4l+3, E <= 256).
 template <bool COHERENT>
 __device__ __forceinline__ void routing_outputs_small(const double *logits, int T, int E, int k, double *lg, int *sel_e,
                                                    double *sel_v, int32_t *idx_out, float *w_out, int32_t *counts,
                                                    int32_t *offsets, int32_t *entries, int32_t *pos) {
     __shared__ int sidx[kSmallT * kMaxTopK];
-    __shared__ int cnt[kRankMaxExperts];
     __shared__ int off_l[kRankMaxExperts];
-    __shared__ int red[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int t = 0; t < T; ++t) {
         topk_block<COHERENT>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
@@ -195,57 +191,61 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
                 sidx[t * k + lane] = sel_e[lane];
             }
         }
-        __syncthreads();
+        if (t + 1 < T) __syncthreads();  // sel_e / sel_v / lg are reused by the next token
     }
-    for (int e = tid; e < E; e += 256) cnt[e] = 0;
-    __syncthreads();
+    if (wave != 0) return;  // the bucket layout is wave 0's alone
+    lds_wave_sync();
     const int S = T * k;
-    int my_e = -1, rank = 0;
-    if (tid < S) {
-        my_e = sidx[tid];
-        for (int q = 0; q < tid; ++q) rank += (sidx[q] == my_e);
-        atomicAdd(&cnt[my_e], 1);
+    // counts of experts 4*lane .. 4*lane + 3
+    int cnt[4] = {0, 0, 0, 0};
+    for (int s = 0; s < S; ++s) {
+        const int e = sidx[s];  // broadcast
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt[i] += (int)(e == 4 * lane + i);
     }
-    __syncthreads();
-    const int c = tid < E ? cnt[tid] : 0;
-    int ctot;
-    const int run = block_exclusive_scan(c, red, &ctot);
-    if (tid < E) {
-        counts[tid] = c;
-        offsets[tid] = run;
-        off_l[tid] = run;
+    const int lsum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    int incl = lsum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
     }
-    if (tid == 0) offsets[E] = ctot;
-    __syncthreads();
-    if (tid < S) {
-        const int p = off_l[my_e] + rank;
-        entries[p] = tid;
-        pos[tid] = p;
+    int run = incl - lsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * lane + i;
+        if (e < E) {
+            counts[e] = cnt[i];
+            offsets[e] = run;
+            off_l[e] = run;
+        }
+        run += cnt[i];
+    }
+    if (lane == 63) offsets[E] = incl;  // = S
+    lds_wave_sync();
+    // pair s: its place in expert e's bucket is the number of earlier pairs of e
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        const int e = s < S ? sidx[s] : -1;
+        int r = 0;
+        for (int q = 0; q < s0 + 64 && q < S; ++q) r += (int)((q < s) & (sidx[q] == e));
+        if (s < S) {
+            const int p = off_l[e] + r;
+            entries[p] = s;
+            pos[s] = p;
+        }
     }
 }
 
-// Router of the small path: logits_small_body's work, then the last
-// workgroup to finish (device-scope counter; the logits travel through
-// agent-scope atomic stores and loads, so no cache maintenance is needed)
-// writes the routing outputs of all T tokens.
-__global__ __launch_bounds__(256) void router_small_kernel(
-    const float *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias, int T, int H, int E,
-    int k, double *__restrict__ logits, f16 *__restrict__ x_hilo, f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
-    uint32_t *__restrict__ counter, int32_t *__restrict__ idx_out, float *__restrict__ w_out,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets, int32_t *__restrict__ entries,
-    int32_t *__restrict__ pos) {
-    logits_small_body<true>(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv);
-    __shared__ int s_last;
-    wait_own_stores();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (counter_arrive(counter) == gridDim.x - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __shared__ __attribute__((aligned(16))) double lg[kRankMaxExperts];
-    __shared__ int sel_e[kMaxTopK];
-    __shared__ double sel_v[kMaxTopK];
-    routing_outputs_small<true>(logits, T, E, k, lg, sel_e, sel_v, idx_out, w_out, counts, offsets, entries, pos);
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Router of the small path: logits (fp64) and the staged x rows. The top-k
+// is recomputed from the logits by every workgroup of the next two launches
+// (each needs only its own token's choice), which is cheaper than handing the
+// choice from workgroup to workgroup.
+__global__ __launch_bounds__(256) void router_small_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+                                                           const float *__restrict__ bias, int T, int H, int E,
+                                                           double *__restrict__ logits, f16 *__restrict__ x_hilo,
+                                                           f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
+    logits_small_body<false>(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv);
 }
 
 constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS
@@ -293,7 +293,7 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
 // of row group rg of expert idx[p] for that single row (MFMA row 0), the four
 // waves splitting the super-blocks. Output h[p][I] = SiLU(gate) * up.
 __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restrict__ GU, int ngroups, int nsb,
-                                                          const int32_t *__restrict__ idx, int k,
+                                                          const double *__restrict__ logits, int E, int k,
                                                           const f16 *__restrict__ x_hilo, const f16 *__restrict__ x_xs,
                                                           const float *__restrict__ x_sinv, float *__restrict__ h,
                                                           int I) {
@@ -301,13 +301,15 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
     __shared__ __attribute__((aligned(16))) f16 axs[kSmallMaxH / kQ4Weights * 16];
     __shared__ float asv[kSmallMaxH / kQ4Weights];
     __shared__ f32x4 red[4][64];
+    __shared__ __attribute__((aligned(16))) double lg[kRankMaxExperts];
+    __shared__ int sel_e[kMaxTopK];
+    __shared__ double sel_v[kMaxTopK];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int p = blockIdx.x, t = p / k, rg = blockIdx.y;
     const int n = lane & 15, g = lane >> 4;
     const int H = nsb * kQ4Weights;
-    const int e = idx[p];  // expert of pair p (one load, in flight with the row copy)
 
-    // token t's staged row
+    // token t's staged row (loads in flight together with the logits)
     {
         const u32x4 *src = (const u32x4 *)(x_hilo + (size_t)t * 2 * H);
         u32x4 *dst = (u32x4 *)arow;
@@ -316,14 +318,14 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
             ((u32x2 *)axs)[c] = ((const u32x2 *)(x_xs + (size_t)t * nsb * 16))[c];
         for (int c = tid; c < nsb; c += 256) asv[c] = x_sinv[(size_t)t * nsb + c];
     }
-    __syncthreads();
-
+    // expert of pair p = t*k + j: slot j of token t's top-k (its barriers also
+    // publish the row copy)
+    topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
+    const int e = sel_e[p - t * k];
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bool a_ok = (n == 0);  // the tile's only row
-    // wave w takes super-blocks w, w+4, ...; two per pass, loads issued first
-    for (int b0 = wave; b0 < nsb; b0 += 8) {
-        u32x4 q0[2], q1[2], hd[2];
+
+    // wave w takes super-blocks w, w+4, ...; two per pass
+    auto load_pass = [&](int b0, u32x4 (&q0)[2], u32x4 (&q1)[2], u32x4 (&hd)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const uint8_t *blk = wg + (size_t)min(b0 + 4 * i, nsb - 1) * kGroupSbBytes;
@@ -331,6 +333,14 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
             q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
             hd[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
         }
+    };
+    u32x4 q0[2], q1[2], hd[2];
+    load_pass(wave, q0, q1, hd);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool a_ok = (n == 0);  // the tile's only row
+    for (int b0 = wave; b0 < nsb; b0 += 8) {
+        if (b0 != wave) load_pass(b0, q0, q1, hd);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int b = b0 + 4 * i;
@@ -359,16 +369,17 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
 constexpr int kDcWaves = 8;        // waves per down/combine workgroup
 constexpr int kDcMaxUnits = 4;     // (slot, super-block) units a wave holds in flight
 
-// Grid (H/16 row groups, T tokens), 512 threads. The k*nsb (slot j,
+// Grid (H/16 row groups + 1, T tokens), 512 threads. The k*nsb (slot j,
 // super-block b) units of one token are spread over the waves; each unit
 // stages its 256 h values (row t*k + j of gateup_pair_kernel's output) in LDS (power-of-two scale, fp16 hi/lo, sub-block
 // sums), runs the row-0 MFMA tile against the down weights of expert idx[t][j]
 // and leaves a 16-column partial in LDS. Then out[t][cols] =
 // sum_j w[t][j] * sum_b partial[j][b] in slot order.
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
-    const uint8_t *__restrict__ Wd, int ngroups, int nsb, const int32_t *__restrict__ idx,
-    const float *__restrict__ w, int k, const float *__restrict__ h, int I,
-    float *__restrict__ out, int H) {
+    const uint8_t *__restrict__ Wd, int ngroups, int nsb, const double *__restrict__ logits, int E, int T, int k,
+    const float *__restrict__ h, int I, float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
+    float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ entries, int32_t *__restrict__ pos) {
     const int rg = blockIdx.x, t = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -377,10 +388,27 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     __shared__ __attribute__((aligned(16))) f16 afrag[kDcWaves][8 * 4 * 16];  // [k-step][g][hi 8 | lo 8]
     __shared__ __attribute__((aligned(16))) f16 axs[kDcWaves][16];
     __shared__ float asinv[kDcWaves];
+    __shared__ __attribute__((aligned(16))) double lg[kRankMaxExperts];
+    __shared__ int sel_e[kMaxTopK];
+    __shared__ double sel_v[kMaxTopK];
 
-    // the token's k experts, lane j holding slot j (one load); h rows are
-    // pair-indexed (t*k + j)
-    const int my_e = idx[(size_t)t * k + min(lane, k - 1)];
+    // The extra column of workgroups (rg == H/16) has no down rows: the first
+    // one writes the routing outputs of all T tokens, the others leave.
+    if (rg == ngroups) {
+        if (t == 0) routing_outputs_small<false>(logits, T, E, k, lg, sel_e, sel_v, idx_out, w_out, counts, offsets,
+                                                 entries, pos);
+        return;
+    }
+    // the token's k experts and renormalised weights, lane j holding slot j;
+    // h rows are pair-indexed (t*k + j)
+    topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
+    const int my_e = sel_e[min(lane, k - 1)];
+    float my_w = 0.f;
+    if (wave == 0) {
+        const double ex = (lane < k) ? exp(sel_v[lane] - sel_v[0]) : 0.0;
+        const double z = wave_sum(ex);
+        my_w = (float)(ex / z);
+    }
     for (int base = 0; base < units; base += kDcWaves * kDcMaxUnits) {
         u32x4 q0[kDcMaxUnits], q1[kDcMaxUnits], hdr[kDcMaxUnits];
         float4 hv[kDcMaxUnits];
@@ -448,14 +476,14 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
         }
     }
     __syncthreads();
-    if (threadIdx.x < 16) {
+    if (wave == 0) {
         float o = 0.f;
         for (int j = 0; j < k; ++j) {
             float y = 0.f;
-            for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][threadIdx.x];
-            o += w[(size_t)t * k + j] * y;
+            for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][lane & 15];
+            o += __shfl(my_w, j, kWave) * y;
         }
-        out[(size_t)t * H + rg * kRowGroup + threadIdx.x] = o;
+        if (lane < 16) out[(size_t)t * H + rg * kRowGroup + lane] = o;
     }
 }
 

@@ -391,12 +391,12 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     Profiler &pf = h->prof;
     if (T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6) {
         // decode path: three launches (see decode.hpp)
-        launch(pf, kStRouter, router_small_kernel, dim3((E + 3) / 4), dim3(256), st, x, h->rw, h->rb, T, H, E, k,
-               w.logits, w.x_hilo, w.x_xs, w.x_sinv, w.rcount, idx, wt, w.counts, w.offsets, w.entries, w.pos);
-        launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(256), st, h->gu, I / 8, nh, idx, k, w.x_hilo,
-               w.x_xs, w.x_sinv, w.h, I);
-        launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup, T), dim3(kDcWaves * 64), st, h->dn,
-               H / kRowGroup, ni, idx, wt, k, w.h, I, out, H);
+        launch(pf, kStRouter, router_small_kernel, dim3((E + 3) / 4), dim3(256), st, x, h->rw, h->rb, T, H, E,
+               w.logits, w.x_hilo, w.x_xs, w.x_sinv);
+        launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(256), st, h->gu, I / 8, nh, w.logits, E, k,
+               w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
+        launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
+               H / kRowGroup, ni, w.logits, E, T, k, w.h, I, out, H, idx, wt, w.counts, w.offsets, w.entries, w.pos);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
         h->last_T = T;
