@@ -176,6 +176,31 @@ class Bench:
         self.layers = []
 
 
+def measured_traffic(kernel: str):
+    """HBM bytes per dispatch of `kernel` from profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    scaled by the plain-copy calibration), or None if not measured or if the kernel's sources changed since."""
+    import hashlib
+    import re
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    k = data["kernels"].get(kernel)
+    if k is None:
+        return None
+    h = hashlib.sha256()
+    for f in k["files"]:
+        h.update(open(os.path.join(here, "quantized_moe_wave_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != k["source_hash"]:
+        return None
+    return int(round((k["fetch_kib"] * data["fetch_factor"] + k["write_kib"] * data["write_factor"]) * 1024))
+
+
 def replicas_for(wl) -> int:
     layer_bytes = wl.experts * wl.expert_bytes + wl.experts * wl.hidden * 4
     return max(1, math.ceil(REPLICA_BYTES / layer_bytes))
@@ -202,8 +227,9 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
             alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * nl for r, _, nl in prof)
             achieved = alg / (total_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "gateup_pair_kernel (gate_up)", "avg_us": round(total_ms / launches * 1e3, 3)}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gateup_pair_kernel"),
+                    "kernel": "gateup_pair_kernel (gate_up)", "avg_us": round(total_ms / launches * 1e3, 3),
+                    "algorithmic_bytes_per_launch": int(round(alg / launches))}
         else:
             # prefill: the gate/up grouped GEMM; 2 * rows * 2I * H flops per launch
             stage = "gate_up_big"
@@ -213,8 +239,10 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
             flops = sum(2.0 * stats[r][2] * 2 * I * H * nl for r, _, nl in prof)
             achieved = flops / (total_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                    "kernel": "expert_gemm_kernel<true> (gate_up_big)", "avg_us": round(total_ms / launches * 1e3, 3)}
+                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic("expert_gemm_kernel<gate_up, 64-row tiles>"),
+                    "kernel": "expert_gemm_kernel<gate_up, 64-row tiles> (gate_up_big)",
+                    "avg_us": round(total_ms / launches * 1e3, 3)}
         avg_us = total_ms / launches * 1e3
         log(f"{wl.name}: {stage} avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")
         if want_stages:
