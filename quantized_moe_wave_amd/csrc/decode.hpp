@@ -59,9 +59,10 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                                                   f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nsb = H / kQ4Weights;
-    const int nw = gridDim.x * 4;
+    const int wpb = blockDim.x >> 6;  // waves per workgroup
+    const int nw = gridDim.x * wpb;
 
-    for (int u = blockIdx.x * 4 + wave; u < T * nsb; u += nw) {
+    for (int u = blockIdx.x * wpb + wave; u < T * nsb; u += nw) {
         const int t = u / nsb, b = u % nsb;
         stage_row_sb(x + (size_t)t * H, nsb, b, x_hilo + (size_t)t * 2 * H, x_xs + (size_t)t * nsb * 16,
                      x_sinv + (size_t)t * nsb);
@@ -69,7 +70,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
 
     // Loads are unconditional (chunk and token indices clamped) so that all of
     // a wave's loads are in flight together; out-of-range terms are skipped.
-    for (int e = blockIdx.x * 4 + wave; e < E; e += nw) {
+    for (int e = blockIdx.x * wpb + wave; e < E; e += nw) {
         double acc[kSmallT];
 #pragma unroll
         for (int t = 0; t < kSmallT; ++t) acc[t] = 0.0;
@@ -241,7 +242,7 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
 // is recomputed from the logits by every workgroup of the next two launches
 // (each needs only its own token's choice), which is cheaper than handing the
 // choice from workgroup to workgroup.
-__global__ __launch_bounds__(256) void router_small_kernel(const float *__restrict__ x, const float *__restrict__ wr,
+__global__ __launch_bounds__(64) void router_small_kernel(const float *__restrict__ x, const float *__restrict__ wr,
                                                            const float *__restrict__ bias, int T, int H, int E,
                                                            double *__restrict__ logits, f16 *__restrict__ x_hilo,
                                                            f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
