@@ -1,69 +1,100 @@
 // Grouped GEMM over expert buckets: tiles of up to 64 rows (RB = 4) for
 // buckets of more than kTileM entries, of up to 16 rows (RB = 1) for smaller.
 //
-// Same arithmetic as expert.hpp (see there for the passages it follows and
-// for the precision scheme): per Q4_K super-block b of the reduction
-// dimension, P = sum_k A_hi*B + A_lo*B on v_mfma_f32_16x16x32_f16 with
-// B = sub-block scale x quant (exact fp16), Q = min-term MFMA, and
-// acc += sinv_row * (d_col * P - dmin_col * Q) in fp32.
+// Arithmetic (expert.hpp cites the passages it follows): over Q4_K
+// super-block b a weight is d_b * sc * q - dmin_b * m, so a weight row's
+// product with an activation row over the super-block is d_b P_b - dmin_b Q_b:
+//   P_b = sum_k A_k (sc q)_k on v_mfma_f32_16x16x32_f16, B = sc q exact in
+//         fp16, A = the staged activation split hi + lo (two MFMAs);
+//   Q_b = sum_j S_j m_j on v_mfma_f32_16x16x16_f16 (S_j the staged 32-column
+//         sums, m_j the 6-bit mins, exact in fp16).
+// The staged activations carry one power-of-two scale s per row, so the
+// result is (1/s) sum_b (d_b P_b - dmin_b Q_b).
 //
-// Work split: a workgroup owns a (16*RB) x 256 output tile: up to 16*RB rows
-// of one expert's bucket (the last tile of a bucket may be partial; its
-// missing rows repeat the last row and are not stored) by 16 repacked 16-row
-// weight groups. Each of its 4 waves computes all rows against 4 weight
-// groups (RB x 4 MFMA tiles). The staged activations cost 4 bytes per element
-// against 0.5625 for Q4_K weights, so the tile is wide in the weight
-// dimension: every staged row fetched serves 256 weight rows, and the 4 waves
-// share it through LDS.
+// One fp32 accumulator X per output holds that sum divided by the current
+// super-block's d: the MFMAs of super-block b add P_b into X, and the
+// super-block boundary applies
+//     X <- (X - (dmin_b / d_b) Q_b) * (d_b / d_{b+1})
+// (after the last super-block the factor is d_b, then 1/s). A super-block row
+// with d = 0 adds only its min term: its B is zeroed and its d taken as 1 in
+// both ratios. Each boundary costs one fp32 rounding, far below the 1e-4 bar
+// over a few dozen super-blocks. One accumulator instead of a per-super-block
+// partial plus a running sum halves the accumulator registers; that is what
+// lets a wave own 64 x 128 outputs.
+//
+// Work split: a workgroup owns a (16*RB) x (64*CW) output tile: up to 16*RB
+// rows of one expert's bucket (the last tile of a bucket may be partial; its
+// missing rows repeat the last row and are not stored) by 4*CW repacked
+// 16-row weight groups. Each of its 4 waves computes all rows against CW
+// weight groups (RB x CW MFMA tiles). A staged activation costs 4 bytes per
+// element against 0.5625 for a Q4_K weight, so the tile is wide in the weight
+// dimension: each staged row fetched serves 64*CW weight rows. The per-CU
+// global->LDS rate (about 23 bytes per cycle on this part) bounds what the
+// MFMAs can be fed: a 64 x 512 tile needs about 16 bytes per cycle of MFMA
+// work, a 64 x 256 tile about 25.
 //
 // Tile order: workgroup L runs on XCD L % 8 (round-robin dispatch). XCD x
 // owns the contiguous range of ceil(n/8) expert tiles starting at x*ceil(n/8)
-// and walks it tile by tile, column block by column block (slot = L / 8 ->
-// tile slot / ncb of the range, column block slot % ncb). The ncb column
-// blocks of a tile run together and share its activation rows through the
-// XCD's L2; tiles are in expert order, so the tiles of one expert run
-// together too and share its weights.
+// and walks it tile by tile, column block by column block. The column blocks
+// of a tile run together and share its activation rows through the XCD's L2;
+// tiles are in expert order, so the tiles of one expert share its weights.
 //
 // Data movement, all by direct global->LDS loads (no staging registers):
-//   A (staged activations): a ring of kGemmRing LDS buffers, each a quarter
-//   super-block (2 k-steps = 256 bytes of each of the 16*RB rows); slot j
-//   of row r is stored at slot j ^ (r % 16) so that the 16 lanes reading one
-//   k-step group of 16 rows hit 16 distinct 16-byte bank groups.
-//   B (repacked quants + headers of the tile's 16 weight groups, 36 KB per
-//   super-block): double-buffered per super-block.
-//   k-step sums and 1/s of every row: double-buffered per super-block.
-// Every wave issues the same loads in the same order, so "chunk c has landed"
-// is a fixed s_waitcnt vmcnt(n) per wave (vmcnt(0) in the last super-block),
-// followed by a barrier.
+//   A (staged activations): a ring of 4 chunk buffers; chunk c = 4b + q is a
+//   quarter super-block (2 k-steps = 256 bytes of each row); 16-byte slot j
+//   of row r is stored at slot j ^ (r % 16), so that the 16 lanes reading one
+//   k-step group of 16 rows hit 16 distinct bank groups.
+//   Bq (quants): a ring of 2 half-super-block buffers (1 KB per weight group;
+//   each wave loads exactly its own CW groups).
+//   HX (headers d, dmin, scales, mins of the tile's groups, and the k-step
+//   sums of its rows): double-buffered per super-block.
+// Per wave, iteration c runs in two halves (k-steps 2q and 2q + 1): the MFMAs
+// of one half run while the fragments of the next are read from LDS and
+// unpacked into the other register set. Between the halves the wave waits for
+// chunk c+1's loads, passes the barrier and issues the group
+//     [HX(b+1) if q == 0] [Bq((c+3)/2) if c is odd] [A(c+4)]
+// into buffers whose last readers have all passed that barrier. Every wave
+// issues the same loads in the same order and they complete in order, so
+// "chunk c+1 has landed" is a fixed vmcnt per q (see the wait below).
 #pragma once
 #include "common.hpp"
 #include "expert.hpp"
 
 namespace moe {
 
-constexpr int kGemmGroups = 16;                             // weight groups per tile (256 columns)
-constexpr int kGemmMinRows = kTileM + 1;                    // buckets this large take 64-row tiles
-constexpr int kChunkBytes = 256;                            // bytes of one row per A chunk (2 k-steps)
-constexpr int kGemmRing = 4;                                // A chunks: one in use, three in flight
+constexpr int kGemmMinRows = kTileM + 1;  // buckets this large take 64-row tiles
+constexpr int kChunkBytes = 256;          // bytes of one row per A chunk (2 k-steps)
+constexpr int kGemmRing = 4;              // A chunk buffers
 static_assert(kGemmRing == 4, "ring slot of chunk 4b + q is q");
-constexpr int kBBufBytes = kGemmGroups * kGroupSbBytes;     // 36 KB
-constexpr int kBLoads = kBBufBytes / (4 * 1024);            // 16-byte loads per lane per super-block: 9
-constexpr int kBXLoads = kBLoads + 2;                       // + k-step sums + 1/s
-constexpr int kXsBufBytes = 4 * 1024;                       // 4 waves x 32 rows x 32 B (rows past the tile repeat)
-constexpr int kSvBufBytes = 4 * 256;                        // 4 waves x 64 floats (waves 1-3 repeat wave 0)
-static_assert(kBBufBytes % (4 * 1024) == 0, "B block must split evenly over 4 waves");
+constexpr int kXsBufBytes = 4 * 1024;     // 4 waves x 32 rows x 32 B (waves 2, 3 repeat 0, 1)
 
-// Tile shape for RB 16-row blocks (RB = 1 or 4).
-template <int RB>
+// Tile shape: RB 16-row blocks, CW 16-column weight groups per wave.
+template <int RB, int CW>
 struct GemmShape {
-    static constexpr int M = 16 * RB;                      // rows per tile
-    static constexpr int ABuf = M * kChunkBytes;           // one A chunk
-    static constexpr int ALoads = ABuf / (4 * 1024);       // 16-byte loads per lane per chunk
-    static constexpr size_t Lds = (size_t)kGemmRing * ABuf + 2 * kBBufBytes + 2 * kXsBufBytes + 2 * kSvBufBytes;
-    static_assert(ABuf % (4 * 1024) == 0, "A chunk must split evenly over 4 waves");
+    static constexpr int M = 16 * RB;                       // rows per tile
+    static constexpr int Groups = 4 * CW;                   // weight groups per tile
+    static constexpr int ABuf = M * kChunkBytes;            // one A chunk
+    static constexpr int ALoads = ABuf / (4 * 1024);        // 16-byte loads per lane per chunk
+    static constexpr int BqBuf = Groups * 1024;             // quants of one half super-block
+    static constexpr int BLoads = BqBuf / (4 * 1024);       // = CW
+    static constexpr int HdrBuf = Groups * 256;             // headers of one super-block
+    static constexpr int HLoads = HdrBuf / (4 * 1024) + 1;  // + the k-step sums
+    static constexpr size_t SvOff =
+        (size_t)kGemmRing * ABuf + 2 * (size_t)BqBuf + 2 * (size_t)HdrBuf + 2 * (size_t)kXsBufBytes;
+    static constexpr size_t Lds = SvOff + 4 * 64 * sizeof(float);  // + 1/s of the rows, one copy per wave
+    // output staging (after the main loop, over the same LDS): M rows of up to
+    // 16 * Groups floats, padded by 4 floats against bank conflicts
+    static constexpr int OutLd = 16 * Groups + 4;
+    static_assert(ABuf % (4 * 1024) == 0 && BqBuf % (4 * 1024) == 0 && HdrBuf % (4 * 1024) == 0,
+                  "buffers must split evenly over 4 waves");
+    static_assert((size_t)M * OutLd * sizeof(float) <= SvOff, "output staging must fit below the 1/s copies");
     static_assert(Lds <= 160 * 1024, "LDS budget");
 };
-constexpr int kGemmM = GemmShape<4>::M;
+constexpr int kGemmM = 64;  // rows of a big tile
+
+// Weight groups per wave for a big tile over ngroups groups (ngroups is a
+// multiple of 16: I/8 for gate/up, H/16 for down).
+__host__ __device__ inline int gemm_cw(int ngroups) { return ngroups % 32 == 0 ? 8 : 4; }
 
 // Upper bound on 64-row tiles for S bucket entries over E experts: each bucket
 // of c >= kGemmMinRows entries takes ceil(c / kGemmM) <= c / kGemmM + 1 tiles.
@@ -89,30 +120,33 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// SiLU with the hardware exp2 and reciprocal (about 2 ulp): z / (1 + e^-z)
+__device__ __forceinline__ float silu_fast(float z) {
+    return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
 // GATEUP: W = repacked gate/up (ngroups = I/8 groups of 8 gate + 8 up rows,
 //   K = H); A rows are the tokens of the bucket entries; out h[slot][I].
 // !GATEUP: W = repacked down (ngroups = H/16, K = I); A rows are the bucket
 //   slots themselves; out Y[slot][H].
-// tiles[t] = (expert, first bucket slot, rows), t < *n_tiles; ncb = ngroups /
-// kGemmGroups column blocks; grid = 8 * ncb * ceil(max tiles / 8).
-template <bool GATEUP, int RB>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void expert_gemm_kernel(const uint8_t *__restrict__ W, int ngroups, int nsb,
-                                                            const int4 *__restrict__ tiles,
-                                                            const int32_t *__restrict__ n_tiles,
-                                                            const int32_t *__restrict__ entries, int k,
-                                                            const f16 *__restrict__ a_hilo,
-                                                            const f16 *__restrict__ a_xs,
-                                                            const float *__restrict__ a_sinv,
-                                                            float *__restrict__ outp, int out_ld) {
-    using Sh = GemmShape<RB>;
-    constexpr int kABufBytes = Sh::ABuf, kALoads = Sh::ALoads;
+// tiles[t] = (expert, first bucket slot, rows), t < *n_tiles. ngroups must be
+// a multiple of 4*CW; ncb = ngroups / (4*CW) column blocks; grid = 8 * ncb *
+// ceil(max tiles / 8). a_sinv holds 1/s of every row (nsb equal entries).
+template <bool GATEUP, int RB, int CW>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void expert_gemm_kernel(
+    const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
+    const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
+    using Sh = GemmShape<RB, CW>;
+    constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *abuf = smem;
-    uint8_t *bbuf = abuf + kGemmRing * kABufBytes;
-    uint8_t *xsbuf = bbuf + 2 * kBBufBytes;
-    float *svbuf = (float *)(xsbuf + 2 * kXsBufBytes);
+    uint8_t *bqbuf = abuf + kGemmRing * Sh::ABuf;
+    uint8_t *hbuf = bqbuf + 2 * Sh::BqBuf;
+    uint8_t *xsbuf = hbuf + 2 * Sh::HdrBuf;
+    float *svbuf = (float *)(smem + Sh::SvOff);
 
-    const int ncb = ngroups / kGemmGroups;
+    const int ncb = ngroups / Sh::Groups;
     const int ntl = *n_tiles;
     const int per_xcd = (ntl + 7) >> 3;  // tiles per XCD (a contiguous range)
     const int slot_id = blockIdx.x >> 3;
@@ -121,10 +155,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (slot_id / ncb >= per_xcd || tile >= ntl) return;
     const u32x4 tr = *(const u32x4 *)&tiles[tile];
     const int e = (int)tr.x, r0 = (int)tr.y, rows = (int)tr.z;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
     const int n = lane & 15, g = lane >> 4;
     const int K = nsb * kQ4Weights;
-    const int rg0 = cblk * kGemmGroups;
+    const int rg0 = cblk * Sh::Groups;
+    const int nchunks = 4 * nsb;
 
     // source row (token for GATEUP, bucket slot otherwise) of tile row r;
     // rows past the end of a partial tile repeat its last row
@@ -133,8 +169,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         return GATEUP ? entries[r0 + rr] / k : r0 + rr;
     };
 
-    // ---- A gather offsets (halves): rows 4*kALoads*wave + 4*i + lane/16, slot
-    // (lane%16) ^ (row%16) of each chunk (staged rows stay far below 2^32 halves)
+    // ---- per-lane load offsets
+    // A (halves): rows 4*kALoads*wave + 4*i + lane/16, slot (lane%16) ^ (row%16)
+    // (staged rows stay far below 2^32 halves)
     uint32_t arow_o[kALoads];
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
@@ -142,70 +179,66 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int sl = (lane & 15) ^ (r & 15);
         arow_o[i] = (uint32_t)src_row(r) * (uint32_t)(2 * K) + (uint32_t)sl * 8u;
     }
-    // k-step sums: rows 32*(wave%2) + lane/2, half (lane&1); 1/s: row lane
-    const f16 *xs_p = a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
-    const float *sv_p = a_sinv + (size_t)src_row(lane) * nsb;
-    // ---- B gather: flat 16-byte slot f = (wave*kBLoads + i)*64 + lane of the
-    // tile's 16 x 2304 bytes of one super-block
+    // Bq: flat 16-byte slot f = (wave*kBLoads + i)*64 + lane of a half
+    // super-block -> group f/64, 16-byte slot f%64 of its 1 KB
     const uint8_t *wtile = W + ((size_t)e * ngroups + rg0) * nsb * kGroupSbBytes;
     uint32_t boff[kBLoads];
 #pragma unroll
     for (int i = 0; i < kBLoads; ++i) {
         const int f = (wave * kBLoads + i) * 64 + lane;
-        boff[i] = (uint32_t)((f / 144) * nsb * kGroupSbBytes + (f % 144) * 16);
+        boff[i] = (uint32_t)((f >> 6) * nsb * kGroupSbBytes + (f & 63) * 16);
     }
+    // headers: flat 16-byte slot f -> group f/16, row f%16 (after the group's
+    // 2 KB of quants)
+    uint32_t hoff[kHLoads - 1];
+#pragma unroll
+    for (int i = 0; i < kHLoads - 1; ++i) {
+        const int f = (wave * (kHLoads - 1) + i) * 64 + lane;
+        hoff[i] = (uint32_t)((f >> 4) * nsb * kGroupSbBytes + kGroupQsBytes + (f & 15) * 16);
+    }
+    // k-step sums: rows 32*(wave%2) + lane/2, half (lane&1)
+    const f16 *xs_p = a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
 
-    auto issue_a = [&](int c) {  // chunk c = 4*b + q into ring buffer c % kGemmRing   (kALoads loads)
+    auto issue_a = [&](int c) {  // chunk c into ring slot c % 4   (kALoads loads)
         const int b = c >> 2, q = c & 3;
-        uint8_t *dst = abuf + (c & (kGemmRing - 1)) * kABufBytes + (4 * kALoads * wave) * kChunkBytes;
+        uint8_t *dst = abuf + (c & (kGemmRing - 1)) * Sh::ABuf + (4 * kALoads * wave) * kChunkBytes;
 #pragma unroll
         for (int i = 0; i < kALoads; ++i) load_lds16(a_hilo + arow_o[i] + b * 512 + q * 128, dst + i * 1024);
     };
-    auto issue_bx = [&](int b) {  // B, k-step sums and 1/s of super-block b   (kBXLoads loads)
-        uint8_t *bd = bbuf + (b & 1) * kBBufBytes + wave * kBLoads * 1024;
+    auto issue_bq = [&](int hs) {  // quants of half super-block hs into slot hs % 2   (kBLoads loads)
+        uint8_t *dst = bqbuf + (hs & 1) * Sh::BqBuf + wave * kBLoads * 1024;
+        const size_t src = (size_t)(hs >> 1) * kGroupSbBytes + (hs & 1) * 1024;
 #pragma unroll
-        for (int i = 0; i < kBLoads; ++i) load_lds16(wtile + boff[i] + (size_t)b * kGroupSbBytes, bd + i * 1024);
+        for (int i = 0; i < kBLoads; ++i) load_lds16(wtile + boff[i] + src, dst + i * 1024);
+    };
+    auto issue_hx = [&](int b) {  // headers + k-step sums of super-block b into buffer b % 2   (kHLoads loads)
+        uint8_t *dst = hbuf + (b & 1) * Sh::HdrBuf + wave * (kHLoads - 1) * 1024;
+#pragma unroll
+        for (int i = 0; i < kHLoads - 1; ++i)
+            load_lds16(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 1024);
         load_lds16(xs_p + b * 16, xsbuf + (b & 1) * kXsBufBytes + wave * 1024);
-        load_lds4(sv_p + b, svbuf + (b & 1) * 256 + 64 * wave);
     };
 
+    // ---- sub-block scales of this lane's CW weight groups (row n) for the
+    // current super-block: bytes 0-3 | 4-7, zero where d = 0 (d, dmin and the
+    // mins are read again at the boundary, while the headers are still in LDS)
+    struct Scales {
+        uint32_t lo[CW], hi[CW];
+    };
+    auto read_scales = [&](int b, Scales &kk) {
+        const uint8_t *hb = hbuf + (b & 1) * Sh::HdrBuf + wave * CW * 256;
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) {
+            const u32x4 hdr = *(const u32x4 *)(hb + cb * 256 + n * 16);
+            const bool live = (hdr.x & 0x7FFFu) != 0u;  // d != 0
+            kk.lo[cb] = live ? (hdr.y & 0x3F3F3F3Fu) : 0u;
+            kk.hi[cb] = live ? ((hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u)) : 0u;
+        }
+    };
     const NibbleConsts nk = nibble_consts();
-    f32x4 acc[RB][4], P[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            P[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-
-    // Per-super-block constants of this lane's 4 weight groups: scales
-    // (bytes 0-3 | 4-7), this lane's 4 mins 4(g%2) .. 4(g%2)+3 (register
-    // values: an array indexed by g%2 would go to scratch), d and dmin.
-    struct SbConsts {
-        uint32_t sc_lo[4], sc_hi[4], mnsel[4];
-        float dd[4], dmin[4];
-    };
-    auto read_consts = [&](int b, SbConsts &k) {
-        const uint8_t *bb = bbuf + (b & 1) * kBBufBytes + wave * 4 * kGroupSbBytes;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const u32x4 hdr = *(const u32x4 *)(bb + cb * kGroupSbBytes + kGroupQsBytes + n * 16);
-            k.sc_lo[cb] = hdr.y & 0x3F3F3F3Fu;
-            k.sc_hi[cb] = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
-            const uint32_t mn_lo = hdr.z & 0x3F3F3F3Fu;
-            const uint32_t mn_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-            k.mnsel[cb] = (g & 1) ? mn_hi : mn_lo;
-            k.dd[cb] = half_bits_to_float(hdr.x & 0xFFFFu);
-            k.dmin[cb] = half_bits_to_float(hdr.x >> 16);
-        }
-    };
-    // Fragments of one half (k-step 2q + s2) of chunk c = 4b + q: the 8 A
-    // fragments (hi, lo of 4 row blocks; ring slot c % 4) and the 4 B
-    // fragments, built from the lane's 8 quant bytes of each of its 4 weight
-    // groups (low nibbles for s2 = 0, high for s2 = 1).
+    // A fragments of half s2 (k-step 2q + s2) of chunk c: hi and lo of RB row blocks
     auto read_a_half = [&](int c, int s2, f16x8 (&Ah)[RB], f16x8 (&Al)[RB]) {
-        const uint8_t *ab = abuf + (c & (kGemmRing - 1)) * kABufBytes;
+        const uint8_t *ab = abuf + (c & (kGemmRing - 1)) * Sh::ABuf;
         const int jh = (s2 * 8 + 2 * g) ^ n;
         const int jl = (s2 * 8 + 2 * g + 1) ^ n;
 #pragma unroll
@@ -215,181 +248,251 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
             Al[rb] = *(const f16x8 *)(ab + r * kChunkBytes + jl * 16);
         }
     };
-    auto read_quants = [&](int c, u32x2 (&w)[4]) {
-        const int q = c & 3;
-        const uint8_t *bb = bbuf + ((c >> 2) & 1) * kBBufBytes + wave * 4 * kGroupSbBytes;
+    // the lane's 8 quant bytes of chunk c in each of its groups: half slot
+    // (c/2) % 2, bytes 8*(c%2) of the lane's 16
+    auto read_quants = [&](int c, u32x2 (&w)[CW]) {
+        const uint8_t *bq = bqbuf + ((c >> 1) & 1) * Sh::BqBuf + wave * CW * 1024;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-            w[cb] = *(const u32x2 *)(bb + cb * kGroupSbBytes + (q >> 1) * 1024 + lane * 16 + (q & 1) * 8);
+        for (int cb = 0; cb < CW; ++cb) w[cb] = *(const u32x2 *)(bq + cb * 1024 + lane * 16 + (c & 1) * 8);
     };
-    auto build_b_half = [&](int q, int s2, const SbConsts &k, const u32x2 (&w)[4], f16x8 (&Bf)[4]) {
+    // B fragments of k-step 2q + s2: sub-block scale x quant (low nibbles for
+    // s2 = 0, high for s2 = 1)
+    auto build_b_half = [&](int q, int s2, const Scales &kk, const u32x2 (&w)[CW], f16x8 (&Bf)[CW]) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const uint32_t scw = q < 2 ? k.sc_lo[cb] : k.sc_hi[cb];
+        for (int cb = 0; cb < CW; ++cb) {
+            const uint32_t scw = q < 2 ? kk.lo[cb] : kk.hi[cb];
             const f16 sc = (f16)(float)((scw >> (16 * (q & 1) + 8 * s2)) & 0xFFu);
             Bf[cb] = s2 ? q_times_scale_nib<1>(w[cb].x, w[cb].y, sc, nk) : q_times_scale_nib<0>(w[cb].x, w[cb].y, sc, nk);
         }
     };
-    auto mfma_half = [&](const f16x8 (&Ah)[RB], const f16x8 (&Al)[RB], const f16x8 (&Bf)[4]) {
+
+    f32x4 X[RB][CW];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) X[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto mfma_half = [&](const f16x8 (&Ah)[RB], const f16x8 (&Al)[RB], const f16x8 (&Bf)[CW]) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-                P[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[rb], Bf[cb], P[rb][cb], 0, 0, 0);
+            for (int cb = 0; cb < CW; ++cb)
+                X[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[rb], Bf[cb], X[rb][cb], 0, 0, 0);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-                P[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[rb], Bf[cb], P[rb][cb], 0, 0, 0);
+            for (int cb = 0; cb < CW; ++cb)
+                X[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[rb], Bf[cb], X[rb][cb], 0, 0, 0);
     };
-    // scheduling pattern of a half (8*RB MFMAs): its LDS reads early, two per
-    // MFMA, then the unpack VALU spread over the rest (masks: 0x100 LDS read,
-    // 0x008 MFMA, 0x002 VALU)
+    // scheduling pattern of a half (2*RB*CW MFMAs): its LDS reads early, two
+    // per MFMA, then the unpack VALU spread over the rest (masks: 0x100 LDS
+    // read, 0x008 MFMA, 0x002 VALU)
     auto interleave = [&]() {
-        constexpr int kDsGroups = RB == 4 ? 6 : 3;
-        constexpr int kValuPer = RB == 4 ? 2 : 8;
+        constexpr int kM = 2 * RB * CW;
+        constexpr int kDs = (2 * RB + CW + 1) / 2;
+        constexpr int kValuPer = (CW * 10 + (kM - kDs) - 1) / (kM - kDs) + 1;
 #pragma unroll
-        for (int i = 0; i < kDsGroups; ++i) {
+        for (int i = 0; i < kDs; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 8 * RB - kDsGroups; ++i) {
+        for (int i = 0; i < kM - kDs; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
         }
     };
-    // the fragments filled in a half must exist at its end (the compiler
-    // would otherwise sink their computation past the next barrier)
-    auto pin = [&](f16x8 (&Ah)[RB], f16x8 (&Al)[RB], f16x8 (&Bf)[4]) {
+    // the B fragments unpacked in a half must exist at its end (the compiler
+    // would otherwise sink their computation past the next barrier); the A
+    // fragments are plain LDS reads and are left unpinned, so that the wait
+    // for them does not get hoisted in front of the MFMAs
+    auto pin = [&](f16x8 (&Bf)[CW]) {
 #pragma unroll
-        for (int j = 0; j < RB; ++j) asm volatile("" : "+v"(Ah[j]), "+v"(Al[j]));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(Bf[j]));
+        for (int j = 0; j < CW; ++j) asm volatile("" : "+v"(Bf[j]));
     };
 
-    // Pipeline (per wave, chunk c = 4b + q, two halves per chunk):
-    //   half 0: MFMAs of (c, k-step 2q) from set 0 | fill set 1 with (c, 2q+1)
-    //   wait until chunk c+1 has landed; barrier; issue BX(b+1) (q == 0;
-    //     before A(4b+4), so that waiting for A(4b+4) covers it) and A(c+4)
-    //     into the ring slot of chunk c, whose last reads were in half 0
-    //   half 1: MFMAs of (c, 2q+1) from set 1 | fill set 0 with (c+1, 2q+2)
-    // Prologue issue order: BX(0), A(0), A(1), A(2), A(3).
-    const int nchunks = 4 * nsb;
-    issue_bx(0);
+    // ---- prologue: 1/s of the tile's rows (row lane, one copy per wave),
+    // then the issue groups of iterations -4 .. -1 (nchunks >= 4):
+    // HX(0) A(0) | Bq(0) A(1) | A(2) | Bq(1) A(3)
+    load_lds4(a_sinv + (size_t)src_row(lane) * nsb, svbuf + wave * 64);
+    issue_hx(0);
+    issue_a(0);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < kGemmRing; ++c) {
-        if (c < nchunks) issue_a(c);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    wait_vm<3 * kALoads>();  // BX(0) and A(0) landed: at most A(1..3) outstanding
+    issue_bq(0);
+    issue_a(1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_bq(1);
+    issue_a(3);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<3 * kALoads + kBLoads>();  // chunk 0 landed: at most A(1), A(2), Bq(1), A(3) in flight
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    SbConsts kc;
-    f16x8 Ah0[RB], Al0[RB], B0[4], Ah1[RB], Al1[RB], B1[4];
-    u32x2 wq[4];
-    read_consts(0, kc);
+    Scales kc;
+    f16x8 Ah0[RB], Al0[RB], B0[CW], Ah1[RB], Al1[RB], B1[CW];
+    u32x2 wq[CW];
+    read_scales(0, kc);
     read_quants(0, wq);
     read_a_half(0, 0, Ah0, Al0);
     build_b_half(0, 0, kc, wq, B0);
     __builtin_amdgcn_sched_barrier(0);
 
     for (int b = 0; b < nsb; ++b) {
-        SbConsts kn;  // constants of super-block b+1 (read at q == 3)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int c = 4 * b + q;
 
-            // half 0
+            // half 0: MFMAs of (c, 2q) from set 0 | fill set 1 with (c, 2q+1)
             read_a_half(c, 1, Ah1, Al1);
             build_b_half(q, 1, kc, wq, B1);
             mfma_half(Ah0, Al0, B0);
             interleave();
-            pin(Ah1, Al1, B1);
+            pin(B1);
             __builtin_amdgcn_sched_barrier(0);
 
-            // At most N loads of this wave issued after A(c+1) are in flight:
-            // A(c+2), A(c+3), and, for q == 1, 2, BX(b+1). Near the end (some
-            // of those never issued) wait for everything.
+            // Chunk c+1 needs A(c+1), Bq((c+1)/2) and, at q == 3, HX(b+1).
+            // What this wave issued after the last of those is the rest of
+            // the issue groups of iterations c-2 | c-1:
+            //   q = 0: A(c+2) | Bq, A(c+3)        q = 1: A(c+2) | HX, A(c+3)
+            //   q = 2: HX, A(c+2) | Bq, A(c+3)    q = 3: A(c+2) | A(c+3)
+            // Once A(c+3) was never issued, some of these are missing: wait
+            // for everything.
             if (c + 3 >= nchunks)
                 wait_vm<0>();
-            else if (q == 1 || q == 2)
-                wait_vm<2 * kALoads + kBXLoads>();
+            else if (q == 0)
+                wait_vm<2 * kALoads + kBLoads>();
+            else if (q == 1)
+                wait_vm<2 * kALoads + kHLoads>();
+            else if (q == 2)
+                wait_vm<2 * kALoads + kHLoads + kBLoads>();
             else
                 wait_vm<2 * kALoads>();
             __builtin_amdgcn_s_waitcnt(0xC07F);  // own LDS reads done before their buffers are refilled
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            if (q == 0 && b + 1 < nsb) issue_bx(b + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (c + kGemmRing < nchunks) issue_a(c + kGemmRing);
+            if (q == 0 && b + 1 < nsb) issue_hx(b + 1);
+            if ((q & 1) && (c + 3) / 2 < 2 * nsb) issue_bq((c + 3) / 2);
+            if (c + 4 < nchunks) issue_a(c + 4);
             __builtin_amdgcn_sched_barrier(0);
 
-            // half 1 (after the last chunk the fill reads stale but in-bounds
-            // LDS and its results go unused; no branch keeps it in one block
-            // with the MFMAs)
+            // half 1: MFMAs of (c, 2q+1) from set 1 | fill set 0 with the
+            // first k-step of chunk c+1. After the last chunk the fill reads
+            // stale but in-bounds LDS and its results go unused (no branch:
+            // it stays in one block with the MFMAs).
             {
-                u32x2 wn[4];
-                if (q == 3) read_consts(b + 1, kn);
+                u32x2 wn[CW];
+                if (q == 3) read_scales(b + 1, kc);
                 read_quants(c + 1, wn);
                 read_a_half(c + 1, 0, Ah0, Al0);
-                build_b_half((q + 1) & 3, 0, q == 3 ? kn : kc, wn, B0);
+                build_b_half((q + 1) & 3, 0, kc, wn, B0);
 #pragma unroll
-                for (int cb = 0; cb < 4; ++cb) wq[cb] = wn[cb];
+                for (int cb = 0; cb < CW; ++cb) wq[cb] = wn[cb];
             }
             mfma_half(Ah1, Al1, B1);
             interleave();
-            pin(Ah0, Al0, B0);
+            pin(B0);
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // super-block b complete: min term and epilogue (its k-step sums and
-        // 1/s sit in buffer b % 2, which BX(b+2) refills only after the next
-        // barrier)
+        // boundary of super-block b: X <- (X - (dmin_b / d_b) Q_b) * f with
+        // f = d_b / d_{b+1}, or d_b after the last super-block. Headers of b
+        // and b+1 and the k-step sums of b are in LDS buffers b % 2 and
+        // (b+1) % 2, which HX(b+2) and HX(b+3) refill only after later
+        // barriers (after the last super-block buffer (b+1) % 2 holds stale
+        // values, which the select drops).
+        const bool last = b + 1 == nsb;
         const uint8_t *xsb = xsbuf + (b & 1) * kXsBufBytes;
-        const float *svb = svbuf + (b & 1) * 256;
+        const uint8_t *hb = hbuf + (b & 1) * Sh::HdrBuf + wave * CW * 256;
+        const uint8_t *hn = hbuf + ((b + 1) & 1) * Sh::HdrBuf + wave * CW * 256;
+        float f[CW], r1[CW];
+        f16x4 Bm[CW];
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) {
+            const u32x4 hdr = *(const u32x4 *)(hb + cb * 256 + n * 16);
+            const uint32_t dn_bits = *(const uint32_t *)(hn + cb * 256 + n * 16);
+            float d = half_bits_to_float(hdr.x & 0xFFFFu);
+            float dnext = half_bits_to_float(dn_bits & 0xFFFFu);
+            d = d != 0.f ? d : 1.f;
+            dnext = (dnext != 0.f && !last) ? dnext : 1.f;
+            // reciprocals to 1 ulp: far below the bar, and no division sequence
+            f[cb] = last ? d : d * __builtin_amdgcn_rcpf(dnext);
+            r1[cb] = half_bits_to_float(hdr.x >> 16) * __builtin_amdgcn_rcpf(d);
+            const uint32_t mn_lo = hdr.z & 0x3F3F3F3Fu;
+            const uint32_t mn_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
+            // this lane's mins 4(g%2) .. 4(g%2)+3 (a select of register
+            // values: an array indexed by g%2 would go to scratch), as fp16:
+            // byte m under exponent byte 0x64 is the half 1024 + m
+            const uint32_t mw = (g & 1) ? mn_hi : mn_lo;
+            const f16x2 k1024 = {(f16)1024.f, (f16)1024.f};
+            const f16x2 m01 = u32_as_f16x2(__builtin_amdgcn_perm(0x64646464u, mw, 0x04010400u)) - k1024;
+            const f16x2 m23 = u32_as_f16x2(__builtin_amdgcn_perm(0x64646464u, mw, 0x04030402u)) - k1024;
+            Bm[cb] = f16x4{m01.x, m01.y, m23.x, m23.y};
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-            const int r = rb * 16 + n;
-            const f16x4 Am = *(const f16x4 *)(xsb + r * 32 + g * 8);
-            const f32x4 sv = *(const f32x4 *)(svb + rb * 16 + 4 * g);  // rows rb*16 + 4g + 0..3
+            const f16x4 Am = *(const f16x4 *)(xsb + (rb * 16 + n) * 32 + g * 8);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const uint32_t mw = kc.mnsel[cb];
-                f16x4 Bm;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Bm[i] = (f16)(float)((mw >> (8 * i)) & 0xFFu);
+            for (int cb = 0; cb < CW; ++cb) {
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const f32x4 Q = __builtin_amdgcn_mfma_f32_16x16x16f16(Am, Bm, zero, 0, 0, 0);
+                const f32x4 Q = __builtin_amdgcn_mfma_f32_16x16x16f16(Am, Bm[cb], zero, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[rb][cb][i] += sv[i] * (kc.dd[cb] * P[rb][cb][i] - kc.dmin[cb] * Q[i]);
-                P[rb][cb] = zero;
+                for (int i = 0; i < 4; ++i) X[rb][cb][i] = (X[rb][cb][i] - r1[cb] * Q[i]) * f[cb];
             }
         }
-        kc = kn;
+        __builtin_amdgcn_sched_barrier(0);
     }
+    wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
 
-    // results: tile rows rb*16 + 4g + i (stored if < rows), columns of weight
-    // group rg0 + 4*wave + cb
+    // results: X of tile rows rb*16 + 4g + i, columns of weight group
+    // CW*wave + cb, times the row's 1/s; staged through LDS (once every wave
+    // is done with the loop's buffers), then written row by row with 16-byte
+    // stores (rows past the end of a partial tile are not stored)
+    float sv[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[rb][i] = svbuf[wave * 64 + rb * 16 + 4 * g + i];
+    __syncthreads();
+    constexpr int OC = GATEUP ? Sh::Groups * 8 : Sh::Groups * kRowGroup;  // output columns of the tile
+    float *stg = (float *)smem;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            const int rg = rg0 + 4 * wave + cb;
+        for (int cb = 0; cb < CW; ++cb) {
+            if (GATEUP) {
+                // lanes n < 8 hold gate, lanes n + 8 up of column n of the
+                // group's 8 h columns. For rows i and i+1 the two lanes swap
+                // one value (gate of row i+1 for up of row i; a DPP rotate
+                // by 8 within each 16-lane row), so that each computes one h:
+                // lane n < 8 row i, lane n + 8 row i+1.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tr_row = rb * 16 + 4 * g + i;
-                const size_t row = (size_t)r0 + tr_row;
-                if (GATEUP) {
-                    const float u = __shfl_xor(acc[rb][cb][i], 8, kWave);
-                    if (n < 8 && tr_row < rows) outp[row * out_ld + rg * 8 + n] = silu_f(acc[rb][cb][i]) * u;
-                } else {
-                    if (tr_row < rows) outp[row * out_ld + rg * kRowGroup + n] = acc[rb][cb][i];
+                for (int i = 0; i < 4; i += 2) {
+                    const float v0 = X[rb][cb][i] * sv[rb][i], v1 = X[rb][cb][i + 1] * sv[rb][i + 1];
+                    const bool gl = n < 8;
+                    const float send = gl ? v1 : v0;
+                    const float recv = __builtin_bit_cast(
+                        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), 0x128, 0xF, 0xF, false));
+                    const float gv = gl ? v0 : recv, uv = gl ? recv : v1;
+                    const int row = rb * 16 + 4 * g + i + (gl ? 0 : 1);
+                    stg[row * Sh::OutLd + (CW * wave + cb) * 8 + (n & 7)] = silu_fast(gv) * uv;
                 }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    stg[(rb * 16 + 4 * g + i) * Sh::OutLd + (CW * wave + cb) * kRowGroup + n] =
+                        X[rb][cb][i] * sv[rb][i];
             }
         }
+    }
+    __syncthreads();
+    constexpr int kV4 = OC / 4;  // 16-byte pieces per row
+    float *obase = outp + (size_t)r0 * out_ld + (size_t)rg0 * (GATEUP ? 8 : kRowGroup);
+    for (int idx = threadIdx.x; idx < Sh::M * kV4; idx += 256) {
+        const int row = idx / kV4, c4 = idx % kV4;
+        if (row < rows)
+            *(f32x4 *)(obase + (size_t)row * out_ld + c4 * 4) = *(const f32x4 *)(stg + row * Sh::OutLd + c4 * 4);
     }
 }
 

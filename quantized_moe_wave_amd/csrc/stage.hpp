@@ -7,20 +7,31 @@
 //     x * s = hi + lo,   hi = fp16(x * s),   lo = fp16(x * s - hi)
 // which keeps ~22 bits. s puts the block's largest |x * s| just under 2^10, so
 // the 32-column sums used for the Q4_K min term stay below 2^15 in fp16 too.
-// The kernels multiply each super-block's partial product by sinv = 1/s, which
-// is exact. Layout: see common.hpp.
-//
-// Grid: one wave per (row, super-block), 4 waves per workgroup. Lanes 0..31
-// each handle one 8-column fragment.
+// The kernels multiply the partial products by sinv = 1/s, which is exact.
+// The decode path scales each super-block on its own; the general path
+// (stage_kernel) uses one scale per row. Layout: see common.hpp.
 #pragma once
 #include "common.hpp"
 
 namespace moe {
 
-// One wave stages super-block b of one row: src points at the row's fp32
-// values (K = nsb*256 columns); lanes 0..31 each own one 8-column fragment.
+// Power-of-two exponent se for a block whose largest magnitude is m:
+// |x * 2^se| < 2^10 (se clamped to +-100; 0 for an all-zero or non-finite m).
+__device__ __forceinline__ int stage_exponent(float m) {
+    int ex = 0;
+    if (m > 0.f) (void)frexpf(m, &ex);  // m < 2^ex
+    int se = 10 - ex;
+    se = se > 100 ? 100 : (se < -100 ? -100 : se);
+    if (!(m > 0.f) || !(m < INFINITY)) se = 0;
+    return se;
+}
+
+// One wave stages super-block b of one row with scale 2^se (se < -1000: use
+// the block's own scale): src points at the row's fp32 values (K = nsb*256
+// columns); lanes 0..31 each own one 8-column fragment.
 __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int nsb, int b, f16 *__restrict__ hilo_row,
-                                             f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+                                             f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
+                                             int se = -10000) {
     const int lane = threadIdx.x & 63;
     const int f = lane & 31;  // fragment: k-step s = f / 4, lane group g = f % 4
     const int s = f >> 2, g = f & 3;
@@ -32,15 +43,12 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
     }
-    float m = 0.f;
+    if (se < -1000) {
+        float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
-    m = wave_max(lane < 32 ? m : 0.f);
-    int ex = 0;
-    if (m > 0.f) (void)frexpf(m, &ex);  // m < 2^ex
-    int se = 10 - ex;
-    se = se > 100 ? 100 : (se < -100 ? -100 : se);
-    if (!(m > 0.f) || !(m < INFINITY)) se = 0;
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        se = stage_exponent(wave_max(lane < 32 ? m : 0.f));
+    }
     const float sc = ldexpf(1.f, se);
 
     f16x8 hi, lo;
@@ -71,15 +79,27 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
     }
 }
 
+// One wave per row, one scale per row (the grouped GEMM applies the row's
+// 1/s once, after its last super-block): the row's largest magnitude sets s,
+// then every super-block is staged with it (same layout as stage_row_sb; the
+// per-super-block 1/s entries all hold the row's value).
 __global__ __launch_bounds__(256) void stage_kernel(const float *__restrict__ src, int rows, int K, int ld_src,
                                                     f16 *__restrict__ hilo, f16 *__restrict__ xs,
                                                     float *__restrict__ sinv) {
     const int nsb = K / kQ4Weights;
-    const long unit = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (unit >= (long)rows * nsb) return;
-    const int row = (int)(unit / nsb), b = (int)(unit % nsb);
-    stage_row_sb(src + (size_t)row * ld_src, nsb, b, hilo + (size_t)row * (2 * K), xs + (size_t)row * nsb * 16,
-                 sinv + (size_t)row * nsb);
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const float *r = src + (size_t)row * ld_src;
+    float m = 0.f;
+    for (int c = lane * 4; c < K; c += 256) {
+        const float4 a = *(const float4 *)(r + c);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    }
+    const int se = stage_exponent(wave_max(m));
+    for (int b = 0; b < nsb; ++b)
+        stage_row_sb(r, nsb, b, hilo + (size_t)row * (2 * K), xs + (size_t)row * nsb * 16, sinv + (size_t)row * nsb,
+                     se);
 }
 
 }  // namespace moe
