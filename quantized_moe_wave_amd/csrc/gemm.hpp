@@ -22,16 +22,18 @@
 // partial plus a running sum halves the accumulator registers; that is what
 // lets a wave own 64 x 128 outputs.
 //
-// Work split: a workgroup owns a (16*RB) x (64*CW) output tile: up to 16*RB
-// rows of one expert's bucket (the last tile of a bucket may be partial; its
-// missing rows repeat the last row and are not stored) by 4*CW repacked
-// 16-row weight groups. Each of its 4 waves computes all rows against CW
+// Work split: a workgroup of NW waves owns a (16*RB) x (16*NW*CW) output
+// tile: up to 16*RB rows of one expert's bucket (the last tile of a bucket
+// may be partial; its missing rows repeat the last row and are not stored) by
+// NW*CW repacked 16-row weight groups. Each wave computes all rows against CW
 // weight groups (RB x CW MFMA tiles). A staged activation costs 4 bytes per
 // element against 0.5625 for a Q4_K weight, so the tile is wide in the weight
-// dimension: each staged row fetched serves 64*CW weight rows. The per-CU
+// dimension: each staged row fetched serves 16*NW*CW weight rows. The per-CU
 // global->LDS rate (about 23 bytes per cycle on this part) bounds what the
 // MFMAs can be fed: a 64 x 512 tile needs about 16 bytes per cycle of MFMA
-// work, a 64 x 256 tile about 25.
+// work, a 64 x 256 tile about 25. Big tiles run 8 waves of 64 x 64 (two per
+// SIMD): while one wave waits (barrier, loads, LDS, the super-block
+// boundary's VALU work) the other keeps the SIMD's matrix unit busy.
 //
 // Tile order: workgroup L runs on XCD L % 8 (round-robin dispatch). XCD x
 // owns the contiguous range of ceil(n/8) expert tiles starting at x*ceil(n/8)
@@ -66,35 +68,39 @@ constexpr int kGemmMinRows = kTileM + 1;  // buckets this large take 64-row tile
 constexpr int kChunkBytes = 256;          // bytes of one row per A chunk (2 k-steps)
 constexpr int kGemmRing = 4;              // A chunk buffers
 static_assert(kGemmRing == 4, "ring slot of chunk 4b + q is q");
-constexpr int kXsBufBytes = 4 * 1024;     // 4 waves x 32 rows x 32 B (waves 2, 3 repeat 0, 1)
 
-// Tile shape: RB 16-row blocks, CW 16-column weight groups per wave.
-template <int RB, int CW>
+// Tile shape: RB 16-row blocks, CW 16-column weight groups per wave, NW waves.
+template <int RB, int CW, int NW>
 struct GemmShape {
+    static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static constexpr int M = 16 * RB;                       // rows per tile
-    static constexpr int Groups = 4 * CW;                   // weight groups per tile
+    static constexpr int Groups = NW * CW;                  // weight groups per tile
     static constexpr int ABuf = M * kChunkBytes;            // one A chunk
-    static constexpr int ALoads = ABuf / (4 * 1024);        // 16-byte loads per lane per chunk
+    static constexpr int ALoads = ABuf / (NW * 1024);       // 16-byte loads per lane per chunk
     static constexpr int BqBuf = Groups * 1024;             // quants of one half super-block
-    static constexpr int BLoads = BqBuf / (4 * 1024);       // = CW
+    static constexpr int BLoads = CW;                       // each wave loads its own groups
     static constexpr int HdrBuf = Groups * 256;             // headers of one super-block
-    static constexpr int HLoads = HdrBuf / (4 * 1024) + 1;  // + the k-step sums
+    // k-step sums of 64 rows x 32 B: 8 waves load 4 bytes per lane; 4 waves
+    // load 16 (rows 32*(wave%2) + lane/2; waves 2, 3 repeat waves 0, 1)
+    static constexpr int XsBuf = NW == 8 ? 2048 : 4096;
+    static constexpr int HLoads = HdrBuf / (NW * 1024) + 1;  // headers + the k-step sums
     static constexpr size_t SvOff =
-        (size_t)kGemmRing * ABuf + 2 * (size_t)BqBuf + 2 * (size_t)HdrBuf + 2 * (size_t)kXsBufBytes;
-    static constexpr size_t Lds = SvOff + 4 * 64 * sizeof(float);  // + 1/s of the rows, one copy per wave
+        (size_t)kGemmRing * ABuf + 2 * (size_t)BqBuf + 2 * (size_t)HdrBuf + 2 * (size_t)XsBuf;
+    static constexpr size_t Lds = SvOff + NW * 64 * sizeof(float);  // + 1/s of the rows, one copy per wave
     // output staging (after the main loop, over the same LDS): M rows of up to
     // 16 * Groups floats, padded by 4 floats against bank conflicts
     static constexpr int OutLd = 16 * Groups + 4;
-    static_assert(ABuf % (4 * 1024) == 0 && BqBuf % (4 * 1024) == 0 && HdrBuf % (4 * 1024) == 0,
-                  "buffers must split evenly over 4 waves");
+    static_assert(ALoads >= 1 && ABuf % (NW * 1024) == 0 && HdrBuf % (NW * 1024) == 0,
+                  "buffers must split evenly over the waves");
     static_assert((size_t)M * OutLd * sizeof(float) <= SvOff, "output staging must fit below the 1/s copies");
     static_assert(Lds <= 160 * 1024, "LDS budget");
 };
 constexpr int kGemmM = 64;  // rows of a big tile
 
-// Weight groups per wave for a big tile over ngroups groups (ngroups is a
-// multiple of 16: I/8 for gate/up, H/16 for down).
-__host__ __device__ inline int gemm_cw(int ngroups) { return ngroups % 32 == 0 ? 8 : 4; }
+// Waves of a big-tile workgroup over ngroups weight groups (a multiple of 16:
+// I/8 for gate/up, H/16 for down): 8 (64 x 512 tiles) where the groups split
+// into blocks of 32, else 4 (64 x 256).
+__host__ __device__ inline int gemm_big_waves(int ngroups) { return ngroups % 32 == 0 ? 8 : 4; }
 
 // Upper bound on 64-row tiles for S bucket entries over E experts: each bucket
 // of c >= kGemmMinRows entries takes ceil(c / kGemmM) <= c / kGemmM + 1 tiles.
@@ -132,12 +138,13 @@ __device__ __forceinline__ float silu_fast(float z) {
 // tiles[t] = (expert, first bucket slot, rows), t < *n_tiles. ngroups must be
 // a multiple of 4*CW; ncb = ngroups / (4*CW) column blocks; grid = 8 * ncb *
 // ceil(max tiles / 8). a_sinv holds 1/s of every row (nsb equal entries).
-template <bool GATEUP, int RB, int CW>
-__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void expert_gemm_kernel(
+template <bool GATEUP, int RB, int CW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void expert_gemm_kernel(
     const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
     const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
-    using Sh = GemmShape<RB, CW>;
+    using Sh = GemmShape<RB, CW, NW>;
+    constexpr int NT = 64 * NW;
     constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *abuf = smem;
@@ -170,7 +177,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     };
 
     // ---- per-lane load offsets
-    // A (halves): rows 4*kALoads*wave + 4*i + lane/16, slot (lane%16) ^ (row%16)
+    // A (halves): rows 4*(kALoads*wave + i) + lane/16, slot (lane%16) ^ (row%16)
     // (staged rows stay far below 2^32 halves)
     uint32_t arow_o[kALoads];
 #pragma unroll
@@ -196,8 +203,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         const int f = (wave * (kHLoads - 1) + i) * 64 + lane;
         hoff[i] = (uint32_t)((f >> 4) * nsb * kGroupSbBytes + kGroupQsBytes + (f & 15) * 16);
     }
-    // k-step sums: rows 32*(wave%2) + lane/2, half (lane&1)
-    const f16 *xs_p = a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
+    // k-step sums: NW == 8: row 8*wave + lane/8, 4-byte piece lane%8;
+    // NW == 4: row 32*(wave%2) + lane/2, 16-byte half lane%2
+    const f16 *xs_p = NW == 8 ? a_xs + (size_t)src_row(8 * wave + (lane >> 3)) * nsb * 16 + (lane & 7) * 2
+                              : a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
 
     auto issue_a = [&](int c) {  // chunk c into ring slot c % 4   (kALoads loads)
         const int b = c >> 2, q = c & 3;
@@ -216,7 +225,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int i = 0; i < kHLoads - 1; ++i)
             load_lds16(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 1024);
-        load_lds16(xs_p + b * 16, xsbuf + (b & 1) * kXsBufBytes + wave * 1024);
+        if (NW == 8)
+            load_lds4(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 256);
+        else
+            load_lds16(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 1024);
     };
 
     // ---- sub-block scales of this lane's CW weight groups (row n) for the
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         // barriers (after the last super-block buffer (b+1) % 2 holds stale
         // values, which the select drops).
         const bool last = b + 1 == nsb;
-        const uint8_t *xsb = xsbuf + (b & 1) * kXsBufBytes;
+        const uint8_t *xsb = xsbuf + (b & 1) * Sh::XsBuf;
         const uint8_t *hb = hbuf + (b & 1) * Sh::HdrBuf + wave * CW * 256;
         const uint8_t *hn = hbuf + ((b + 1) & 1) * Sh::HdrBuf + wave * CW * 256;
         float f[CW], r1[CW];
@@ -489,7 +501,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __syncthreads();
     constexpr int kV4 = OC / 4;  // 16-byte pieces per row
     float *obase = outp + (size_t)r0 * out_ld + (size_t)rg0 * (GATEUP ? 8 : kRowGroup);
-    for (int idx = threadIdx.x; idx < Sh::M * kV4; idx += 256) {
+    for (int idx = threadIdx.x; idx < Sh::M * kV4; idx += NT) {
         const int row = idx / kV4, c4 = idx % kV4;
         if (row < rows)
             *(f32x4 *)(obase + (size_t)row * out_ld + c4 * 4) = *(const f32x4 *)(stg + row * Sh::OutLd + c4 * 4);

@@ -307,20 +307,20 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
     hipStream_t hs = (hipStream_t)stream;
     {
         const hipError_t a[5] = {
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4>::Lds)};
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds)};
         for (hipError_t e : a)
             if (e != hipSuccess)
                 return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
-                            GemmShape<4, 8>::Lds, hipGetErrorString(e));
+                            GemmShape<4, 4, 8>::Lds, hipGetErrorString(e));
     }
     moe_ffn_t h = new moe_ffn_s();
     h->sh = s;
@@ -421,37 +421,37 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
            w.x_sinv);
 
     // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
-    // (see gemm.hpp); 16-row x 256-column tiles for buckets of at most 16
-    // entries, 64-row x 512-column (or 256 where the weight groups do not
-    // split into 512-column blocks) for larger ones.
+    // (see gemm.hpp); 16-row x 256-column tiles (4 waves) for buckets of at
+    // most 16 entries, 64-row x 512-column tiles (8 waves) for larger ones, or
+    // 64 x 256 (4 waves) where the weight groups do not split into blocks of 32.
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
     const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
-    using Small = GemmShape<1, 4>;
-    using Big = GemmShape<4, 8>;
-    using BigN = GemmShape<4, 4>;
-    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4>, dim3(8 * (gu_groups / Small::Groups) * ms8),
+    using Small = GemmShape<1, 4, 4>;
+    using Big = GemmShape<4, 4, 8>;
+    using BigN = GemmShape<4, 4, 4>;
+    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4, 4>, dim3(8 * (gu_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
                w.x_xs, w.x_sinv, w.h, I);
     if (S >= kGemmMinRows)
-        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
-                   dim3(256), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
+        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 4, 8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
+                   dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
                    w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
 
     launch(pf, kStStageH, stage_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo, w.h_xs,
            w.h_sinv);
 
-    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4>, dim3(8 * (dn_groups / Small::Groups) * ms8),
+    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4, 4>, dim3(8 * (dn_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
                w.h_xs, w.h_sinv, w.Y, H);
     if (S >= kGemmMinRows) {
-        if (gemm_cw(dn_groups) == 8)
-            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 8>, dim3(8 * (dn_groups / Big::Groups) * mg8),
-                       dim3(256), Big::Lds, st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k,
-                       w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
+        if (gemm_big_waves(dn_groups) == 8)
+            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8>,
+                       dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
         else
-            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4>, dim3(8 * (dn_groups / BigN::Groups) * mg8),
-                       dim3(256), BigN::Lds, st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k,
-                       w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
+            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 4>,
+                       dim3(8 * (dn_groups / BigN::Groups) * mg8), dim3(256), BigN::Lds, st, h->dn, dn_groups, ni,
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
     }
 
     launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
