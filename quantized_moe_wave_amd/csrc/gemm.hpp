@@ -12,15 +12,14 @@
 // result is (1/s) sum_b (d_b P_b - dmin_b Q_b).
 //
 // One fp32 accumulator X per output holds that sum divided by the current
-// super-block's d: the MFMAs of super-block b add P_b into X, and the
-// super-block boundary applies
-//     X <- (X - (dmin_b / d_b) Q_b) * (d_b / d_{b+1})
-// (after the last super-block the factor is d_b, then 1/s). A super-block row
-// with d = 0 adds only its min term: its B is zeroed and its d taken as 1 in
-// both ratios. Each boundary costs one fp32 rounding, far below the 1e-4 bar
-// over a few dozen super-blocks. One accumulator instead of a per-super-block
-// partial plus a running sum halves the accumulator registers; that is what
-// lets a wave own 64 x 128 outputs.
+// super-block's d: during super-block b its MFMAs add P_b into X and its min
+// term adds -(dmin_b / d_b) Q_b (at any point of b, X being in units of d_b
+// throughout); between b and b+1, X is multiplied by d_b / d_{b+1} (after the
+// last super-block by d_b, then by 1/s). A super-block row with d = 0 adds
+// only its min term: its B is zeroed and its d taken as 1 in both ratios.
+// Each rescale costs one fp32 rounding, far below the 1e-4 bar over a few
+// dozen super-blocks. One accumulator instead of a per-super-block partial
+// plus a running sum halves the accumulator registers.
 //
 // Work split: a workgroup of NW waves owns a (16*RB) x (16*NW*CW) output
 // tile: up to 16*RB rows of one expert's bucket (the last tile of a bucket
@@ -59,6 +58,8 @@
 // issues the same loads in the same order and they complete in order, so
 // "chunk c+1 has landed" is a fixed vmcnt per q (see the wait below).
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 #include "expert.hpp"
 
@@ -167,7 +168,6 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     const int n = lane & 15, g = lane >> 4;
     const int K = nsb * kQ4Weights;
     const int rg0 = cblk * Sh::Groups;
-    const int nchunks = 4 * nsb;
 
     // source row (token for GATEUP, bucket slot otherwise) of tile row r;
     // rows past the end of a partial tile repeat its last row
@@ -297,12 +297,15 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 X[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[rb], Bf[cb], X[rb][cb], 0, 0, 0);
     };
     // scheduling pattern of a half (2*RB*CW MFMAs): its LDS reads early, two
-    // per MFMA, then the unpack VALU spread over the rest (masks: 0x100 LDS
-    // read, 0x008 MFMA, 0x002 VALU)
-    auto interleave = [&]() {
+    // per MFMA, then the unpack VALU spread over the rest, and nld global->LDS
+    // loads spread evenly among those MFMAs so that the load pipe is fed
+    // steadily instead of in one burst (masks: 0x100 LDS read, 0x008 MFMA,
+    // 0x002 VALU, 0x020 global load)
+    auto interleave = [&](int nld) {
         constexpr int kM = 2 * RB * CW;
         constexpr int kDs = (2 * RB + CW + 1) / 2;
         constexpr int kValuPer = (CW * 10 + (kM - kDs) - 1) / (kM - kDs) + 1;
+        const int every = nld > 0 ? (kM - kDs) / nld : kM;
 #pragma unroll
         for (int i = 0; i < kDs; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -312,6 +315,7 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
         for (int i = 0; i < kM - kDs; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
+            if (nld > 0 && i % every == every - 1 && i / every < nld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
     };
     // the B fragments unpacked in a half must exist at its end (the compiler
@@ -351,85 +355,27 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     build_b_half(0, 0, kc, wq, B0);
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int b = 0; b < nsb; ++b) {
+    // Super-block b's min term and its rescale are spread over its
+    // iterations (the accumulator is in units of d_b all through b):
+    //   q = 1, half 0: X -= (dmin_b / d_b) Q_b   (Q_b on the k-step sums;
+    //                  the headers and sums of b stay in LDS until HX(b+2))
+    //   q = 3, half 1: f = d_b / d_{b+1} (d_last after the last super-block)
+    //   next q = 0, half 0: X *= f, tile by tile ahead of its MFMAs
+    // A d of 0 counts as 1 (its scales are zeroed, only the min term is left).
+    float fcur[CW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 4 * b + q;
-
-            // half 0: MFMAs of (c, 2q) from set 0 | fill set 1 with (c, 2q+1)
-            read_a_half(c, 1, Ah1, Al1);
-            build_b_half(q, 1, kc, wq, B1);
-            mfma_half(Ah0, Al0, B0);
-            interleave();
-            pin(B1);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // Chunk c+1 needs A(c+1), Bq((c+1)/2) and, at q == 3, HX(b+1).
-            // What this wave issued after the last of those is the rest of
-            // the issue groups of iterations c-2 | c-1:
-            //   q = 0: A(c+2) | Bq, A(c+3)        q = 1: A(c+2) | HX, A(c+3)
-            //   q = 2: HX, A(c+2) | Bq, A(c+3)    q = 3: A(c+2) | A(c+3)
-            // Once A(c+3) was never issued, some of these are missing: wait
-            // for everything.
-            if (c + 3 >= nchunks)
-                wait_vm<0>();
-            else if (q == 0)
-                wait_vm<2 * kALoads + kBLoads>();
-            else if (q == 1)
-                wait_vm<2 * kALoads + kHLoads>();
-            else if (q == 2)
-                wait_vm<2 * kALoads + kHLoads + kBLoads>();
-            else
-                wait_vm<2 * kALoads>();
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // own LDS reads done before their buffers are refilled
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            if (q == 0 && b + 1 < nsb) issue_hx(b + 1);
-            if ((q & 1) && (c + 3) / 2 < 2 * nsb) issue_bq((c + 3) / 2);
-            if (c + 4 < nchunks) issue_a(c + 4);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // half 1: MFMAs of (c, 2q+1) from set 1 | fill set 0 with the
-            // first k-step of chunk c+1. After the last chunk the fill reads
-            // stale but in-bounds LDS and its results go unused (no branch:
-            // it stays in one block with the MFMAs).
-            {
-                u32x2 wn[CW];
-                if (q == 3) read_scales(b + 1, kc);
-                read_quants(c + 1, wn);
-                read_a_half(c + 1, 0, Ah0, Al0);
-                build_b_half((q + 1) & 3, 0, kc, wn, B0);
-#pragma unroll
-                for (int cb = 0; cb < CW; ++cb) wq[cb] = wn[cb];
-            }
-            mfma_half(Ah1, Al1, B1);
-            interleave();
-            pin(B0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // boundary of super-block b: X <- (X - (dmin_b / d_b) Q_b) * f with
-        // f = d_b / d_{b+1}, or d_b after the last super-block. Headers of b
-        // and b+1 and the k-step sums of b are in LDS buffers b % 2 and
-        // (b+1) % 2, which HX(b+2) and HX(b+3) refill only after later
-        // barriers (after the last super-block buffer (b+1) % 2 holds stale
-        // values, which the select drops).
-        const bool last = b + 1 == nsb;
+    for (int cb = 0; cb < CW; ++cb) fcur[cb] = 1.f;
+    auto min_term = [&](int b) {
         const uint8_t *xsb = xsbuf + (b & 1) * Sh::XsBuf;
         const uint8_t *hb = hbuf + (b & 1) * Sh::HdrBuf + wave * CW * 256;
-        const uint8_t *hn = hbuf + ((b + 1) & 1) * Sh::HdrBuf + wave * CW * 256;
-        float f[CW], r1[CW];
+        float r1[CW];
         f16x4 Bm[CW];
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
             const u32x4 hdr = *(const u32x4 *)(hb + cb * 256 + n * 16);
-            const uint32_t dn_bits = *(const uint32_t *)(hn + cb * 256 + n * 16);
             float d = half_bits_to_float(hdr.x & 0xFFFFu);
-            float dnext = half_bits_to_float(dn_bits & 0xFFFFu);
             d = d != 0.f ? d : 1.f;
-            dnext = (dnext != 0.f && !last) ? dnext : 1.f;
-            // reciprocals to 1 ulp: far below the bar, and no division sequence
-            f[cb] = last ? d : d * __builtin_amdgcn_rcpf(dnext);
+            // reciprocal to 1 ulp: far below the bar, and no division sequence
             r1[cb] = half_bits_to_float(hdr.x >> 16) * __builtin_amdgcn_rcpf(d);
             const uint32_t mn_lo = hdr.z & 0x3F3F3F3Fu;
             const uint32_t mn_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
@@ -450,15 +396,103 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 Q = __builtin_amdgcn_mfma_f32_16x16x16f16(Am, Bm[cb], zero, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) X[rb][cb][i] = (X[rb][cb][i] - r1[cb] * Q[i]) * f[cb];
+                for (int i = 0; i < 4; ++i) X[rb][cb][i] -= r1[cb] * Q[i];
             }
         }
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    auto next_factor = [&](int b, bool last) {
+        const uint8_t *hb = hbuf + (b & 1) * Sh::HdrBuf + wave * CW * 256;
+        const uint8_t *hn = hbuf + ((b + 1) & 1) * Sh::HdrBuf + wave * CW * 256;
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) {
+            float d = half_bits_to_float(*(const uint32_t *)(hb + cb * 256 + n * 16) & 0xFFFFu);
+            float dn = half_bits_to_float(*(const uint32_t *)(hn + cb * 256 + n * 16) & 0xFFFFu);
+            d = d != 0.f ? d : 1.f;
+            dn = (dn != 0.f && !last) ? dn : 1.f;  // after the last super-block: stale LDS, dropped
+            fcur[cb] = d * __builtin_amdgcn_rcpf(dn);
+        }
+    };
+
+    // One super-block: 4 iterations. LOADS: every load of the issue groups
+    // exists (b < nsb - 1), so each wait is a fixed count and the groups are
+    // spread over the MFMAs of half 1. The last super-block issues nothing.
+    auto sb_step = [&](int b, auto loads_tag) {
+        constexpr bool LOADS = decltype(loads_tag)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 4 * b + q;
+
+            // half 0: MFMAs of (c, 2q) from set 0 | fill set 1 with (c, 2q+1)
+            if (q == 0) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < CW; ++cb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) X[rb][cb][i] *= fcur[cb];
+            }
+            if (q == 1) min_term(b);
+            read_a_half(c, 1, Ah1, Al1);
+            build_b_half(q, 1, kc, wq, B1);
+            mfma_half(Ah0, Al0, B0);
+            interleave(0);
+            pin(B1);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // Chunk c+1 needs A(c+1), Bq((c+1)/2) and, at q == 3, HX(b+1).
+            // What this wave issued after the last of those is the rest of
+            // the issue groups of iterations c-2 | c-1:
+            //   q = 0: A(c+2) | Bq, A(c+3)        q = 1: A(c+2) | HX, A(c+3)
+            //   q = 2: HX, A(c+2) | Bq, A(c+3)    q = 3: A(c+2) | A(c+3)
+            // In the last super-block (no loads) those groups are complete
+            // only for q = 0; later waits take everything.
+            if (q == 0)
+                wait_vm<2 * kALoads + kBLoads>();
+            else if (!LOADS)
+                wait_vm<0>();
+            else if (q == 1)
+                wait_vm<2 * kALoads + kHLoads>();
+            else if (q == 2)
+                wait_vm<2 * kALoads + kHLoads + kBLoads>();
+            else
+                wait_vm<2 * kALoads>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // own LDS reads done before their buffers are refilled
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+
+            // half 1: MFMAs of (c, 2q+1) from set 1 | fill set 0 with the
+            // first k-step of chunk c+1 | the issue group of iteration c.
+            // After the last chunk the fill reads stale but in-bounds LDS
+            // and its results go unused.
+            {
+                u32x2 wn[CW];
+                if (q == 3) {
+                    read_scales(b + 1, kc);
+                    next_factor(b, !LOADS);
+                }
+                read_quants(c + 1, wn);
+                read_a_half(c + 1, 0, Ah0, Al0);
+                build_b_half((q + 1) & 3, 0, kc, wn, B0);
+#pragma unroll
+                for (int cb = 0; cb < CW; ++cb) wq[cb] = wn[cb];
+            }
+            if constexpr (LOADS) {
+                if (q == 0) issue_hx(b + 1);
+                if (q & 1) issue_bq((c + 3) / 2);
+                issue_a(c + 4);
+            }
+            mfma_half(Ah1, Al1, B1);
+            interleave(!LOADS ? 0 : q == 0 ? kHLoads + kALoads : q == 2 ? kALoads : kBLoads + kALoads);
+            pin(B0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    for (int b = 0; b < nsb - 1; ++b) sb_step(b, std::integral_constant<bool, true>{});
+    sb_step(nsb - 1, std::integral_constant<bool, false>{});
     wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
 
     // results: X of tile rows rb*16 + 4g + i, columns of weight group
-    // CW*wave + cb, times the row's 1/s; staged through LDS (once every wave
+    // CW*wave + cb, times d of the last super-block and the row's 1/s; staged through LDS (once every wave
     // is done with the loop's buffers), then written row by row with 16-byte
     // stores (rows past the end of a partial tile are not stored)
     float sv[RB][4];
@@ -481,7 +515,8 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
                 // lane n < 8 row i, lane n + 8 row i+1.
 #pragma unroll
                 for (int i = 0; i < 4; i += 2) {
-                    const float v0 = X[rb][cb][i] * sv[rb][i], v1 = X[rb][cb][i + 1] * sv[rb][i + 1];
+                    const float v0 = X[rb][cb][i] * (fcur[cb] * sv[rb][i]);
+                    const float v1 = X[rb][cb][i + 1] * (fcur[cb] * sv[rb][i + 1]);
                     const bool gl = n < 8;
                     const float send = gl ? v1 : v0;
                     const float recv = __builtin_bit_cast(
@@ -494,7 +529,7 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     stg[(rb * 16 + 4 * g + i) * Sh::OutLd + (CW * wave + cb) * kRowGroup + n] =
-                        X[rb][cb][i] * sv[rb][i];
+                        X[rb][cb][i] * (fcur[cb] * sv[rb][i]);
             }
         }
     }
