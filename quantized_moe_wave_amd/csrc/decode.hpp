@@ -48,10 +48,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
     return before + x - v;
 }
 
-// ceil(E/4) workgroups of 256 threads, one expert per wave; every workgroup
-// also stages a share of the T x super-block units of x. COHERENT: logits are
-// stored with agent-scope atomic stores (read back by another workgroup of
-// the same launch).
+// One wave per expert (waves 0 .. E-1 of the grid) and one per (token,
+// super-block) staging unit of x (the T*nsb waves after them), so that no
+// wave does both one after the other. COHERENT: logits are stored with
+// agent-scope atomic stores (read back by another workgroup of the same
+// launch).
 template <bool COHERENT>
 __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, const float *__restrict__ wr,
                                                   const float *__restrict__ bias, int T, int H, int E,
@@ -62,7 +63,8 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
     const int wpb = blockDim.x >> 6;  // waves per workgroup
     const int nw = gridDim.x * wpb;
 
-    for (int u = blockIdx.x * wpb + wave; u < T * nsb; u += nw) {
+    for (int u = blockIdx.x * wpb + wave - E; u < T * nsb; u += nw) {
+        if (u < 0) break;  // an expert wave
         const int t = u / nsb, b = u % nsb;
         stage_row_sb(x + (size_t)t * H, nsb, b, x_hilo + (size_t)t * 2 * H, x_xs + (size_t)t * nsb * 16,
                      x_sinv + (size_t)t * nsb);
@@ -238,7 +240,8 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
     }
 }
 
-// Router of the small path: logits (fp64) and the staged x rows. The top-k
+// Router of the small path: logits (fp64) and the staged x rows; grid of
+// E + T*nsb one-wave workgroups. The top-k
 // is recomputed from the logits by every workgroup of the next two launches
 // (each needs only its own token's choice), which is cheaper than handing the
 // choice from workgroup to workgroup.
@@ -310,19 +313,24 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
     const int n = lane & 15, g = lane >> 4;
     const int H = nsb * kQ4Weights;
 
-    // token t's staged row (loads in flight together with the logits)
-    {
-        const u32x4 *src = (const u32x4 *)(x_hilo + (size_t)t * 2 * H);
-        u32x4 *dst = (u32x4 *)arow;
-        for (int c = tid; c < H / 4; c += 256) dst[c] = src[c];
-        for (int c = tid; c < nsb * 4; c += 256)
-            ((u32x2 *)axs)[c] = ((const u32x2 *)(x_xs + (size_t)t * nsb * 16))[c];
-        for (int c = tid; c < nsb; c += 256) asv[c] = x_sinv[(size_t)t * nsb + c];
-    }
-    // expert of pair p = t*k + j: slot j of token t's top-k (its barriers also
-    // publish the row copy)
+    // token t's staged row: loaded into registers first, so that these loads
+    // and the top-k's logit loads are in flight together; stored to LDS after
+    constexpr int kRowLoads = kSmallMaxH / 4 / 256;  // 16-byte pieces per thread
+    u32x4 xr[kRowLoads];
+    const u32x4 *xsrc = (const u32x4 *)(x_hilo + (size_t)t * 2 * H);
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i) xr[i] = xsrc[min(tid + 256 * i, H / 4 - 1)];
+    const u32x2 xsr = ((const u32x2 *)(x_xs + (size_t)t * nsb * 16))[min(tid, nsb * 4 - 1)];
+    const float svr = x_sinv[(size_t)t * nsb + min(tid, nsb - 1)];
+    // expert of pair p = t*k + j: slot j of token t's top-k
     topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
     const int e = sel_e[p - t * k];
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i)
+        if (tid + 256 * i < H / 4) ((u32x4 *)arow)[tid + 256 * i] = xr[i];
+    if (tid < nsb * 4) ((u32x2 *)axs)[tid] = xsr;
+    if (tid < nsb) asv[tid] = svr;
+    __syncthreads();
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
 
     // wave w takes super-blocks w, w+4, ...; two per pass
@@ -400,8 +408,16 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
                                                  entries, pos);
         return;
     }
-    // the token's k experts and renormalised weights, lane j holding slot j;
-    // h rows are pair-indexed (t*k + j)
+    // h rows are pair-indexed (t*k + j), so the first pass's h loads do not
+    // wait for the top-k: issued here, they are in flight with its logit loads
+    float4 hv0[kDcMaxUnits];
+#pragma unroll
+    for (int i = 0; i < kDcMaxUnits; ++i) {
+        const int u = min(i * kDcWaves + wave, units - 1);
+        const int j = u / nsb, b = u % nsb;
+        hv0[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
+    }
+    // the token's k experts and renormalised weights, lane j holding slot j
     topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
     const int my_e = sel_e[min(lane, k - 1)];
     float my_w = 0.f;
@@ -422,7 +438,10 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
             q0[i] = *(const u32x4 *)(blk + lane * 16);
             q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
             hdr[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
-            hv[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
+            if (base == 0)
+                hv[i] = hv0[i];
+            else
+                hv[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
         }
 #pragma unroll
         for (int i = 0; i < kDcMaxUnits; ++i) {

@@ -393,7 +393,7 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     Profiler &pf = h->prof;
     if (T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6) {
         // decode path: three launches (see decode.hpp)
-        launch(pf, kStRouter, router_small_kernel, dim3(E), dim3(64), st, x, h->rw, h->rb, T, H, E,
+        launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
                w.logits, w.x_hilo, w.x_xs, w.x_sinv);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(256), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
