@@ -17,7 +17,8 @@
 //
 // Grid: E workgroups (one per expert), 256 threads. Every workgroup builds the
 // full histogram in LDS (integer atomics only), so no workgroup waits for
-// another.
+// another. Each thread holds runs of kBkPairs consecutive pairs in registers,
+// loaded in one go, so a round costs one memory round trip.
 #pragma once
 #include "common.hpp"
 #include "gemm.hpp"
@@ -27,6 +28,8 @@ namespace moe {
 // GEMM tiles and 16-row tiles of a bucket of c entries.
 __device__ __forceinline__ int gemm_tiles_of(int c) { return c >= kGemmMinRows ? (c + kGemmM - 1) / kGemmM : 0; }
 __device__ __forceinline__ int small_tiles_of(int c) { return c >= kGemmMinRows ? 0 : (c + kTileM - 1) / kTileM; }
+
+constexpr int kBkPairs = 32;  // consecutive (token, slot) pairs per thread per round
 
 __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
                                                      int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
@@ -39,10 +42,37 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int e = blockIdx.x;
     const int S = T * k;
+    constexpr int kRound = 256 * kBkPairs;
+
+    // this thread's pairs of a round, loaded together (16 bytes at a time
+    // where aligned; pairs past S read as -1)
+    const bool vec_ok = ((uintptr_t)idx & 15u) == 0;  // the caller's array may be only 4-byte aligned
+    auto load_pairs = [&](int r0, int (&v)[kBkPairs]) {
+        const int s0 = r0 + tid * kBkPairs;
+#pragma unroll
+        for (int i = 0; i < kBkPairs; i += 4) {
+            if (vec_ok && s0 + i + 3 < S) {
+                const int4 q = *(const int4 *)&idx[s0 + i];
+                v[i] = q.x;
+                v[i + 1] = q.y;
+                v[i + 2] = q.z;
+                v[i + 3] = q.w;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[i + j] = s0 + i + j < S ? idx[s0 + i + j] : -1;
+            }
+        }
+    };
 
     for (int i = tid; i < E; i += 256) cnt[i] = 0;
     __syncthreads();
-    for (int s = tid; s < S; s += 256) atomicAdd(&cnt[idx[s]], 1);
+    for (int r0 = 0; r0 < S; r0 += kRound) {
+        int v[kBkPairs];
+        load_pairs(r0, v);
+#pragma unroll
+        for (int i = 0; i < kBkPairs; ++i)
+            if (v[i] >= 0) atomicAdd(&cnt[v[i]], 1);
+    }
     __syncthreads();
 
     // Entries and tiles below expert e.
@@ -96,29 +126,40 @@ __global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__
         tiles[toff + i] = make_int4(e, off + i * kTileM, min(kTileM, mine - i * kTileM), 0);
     if (mine == 0) return;
 
-    // Stable scatter: tokens in ascending order, 256 per pass.
+    // Stable scatter: pairs in index order (= token order, a token choosing e
+    // at most once). Each thread counts e among its consecutive pairs, a
+    // workgroup scan places them, and the thread writes its matches in order.
+    __syncthreads();  // wave_tot is reused below
     int base = off;
-    for (int t0 = 0; t0 < T; t0 += 256) {
-        const int t = t0 + tid;
-        int j = -1;
-        if (t < T) {
-            for (int jj = 0; jj < k; ++jj)
-                if (idx[(size_t)t * k + jj] == e) j = jj;
+    for (int r0 = 0; r0 < S; r0 += kRound) {
+        int v[kBkPairs];
+        load_pairs(r0, v);
+        int m = 0;
+#pragma unroll
+        for (int i = 0; i < kBkPairs; ++i) m += (int)(v[i] == e);
+        int incl = m;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += y;
         }
-        const bool flag = j >= 0;
-        const uint64_t ball = __ballot(flag);
-        const int rank_in_wave = __popcll(ball & ((1ull << lane) - 1ull));
+        if (lane == 63) wave_tot[0][wave] = incl;
         __syncthreads();
-        if (lane == 0) wave_tot[0][wave] = __popcll(ball);
-        __syncthreads();
-        int before = 0;
+        int before = incl - m;
         for (int w = 0; w < wave; ++w) before += wave_tot[0][w];
-        if (flag) {
-            const int p = base + before + rank_in_wave;
-            entries[p] = t * k + j;
-            pos[(size_t)t * k + j] = p;
+        const int total = wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
+        int p = base + before;
+        const int s0 = r0 + tid * kBkPairs;
+#pragma unroll
+        for (int i = 0; i < kBkPairs; ++i) {
+            if (v[i] == e) {
+                entries[p] = s0 + i;
+                pos[s0 + i] = p;
+                ++p;
+            }
         }
-        base += wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
+        base += total;
+        __syncthreads();  // wave_tot is rewritten by the next round
     }
 }
 

@@ -32,7 +32,7 @@ constexpr int kRankMaxExperts = 256;  // rank-based selection up to this many ex
 // their slot. Same result as k rounds of argmax with the lower-index rule, in
 // fp64, without a serial chain of cross-lane steps. lds: this wave's scratch
 // of kRankMaxExperts + kMaxTopK doubles + kMaxTopK ints.
-template <int PL>
+template <int PL, bool COHERENT = true>
 __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
                                                int *sidx, double *lds) {
     const int lane = threadIdx.x & 63;
@@ -40,7 +40,9 @@ __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k,
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int c = lane + 64 * i;
-        const double x = __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // COHERENT: the logits were written by other workgroups of this launch
+        const double x = COHERENT ? __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                  : lrow[min(c, E - 1)];
         v[i] = (c < E && x == x) ? x : -INFINITY;  // NaN never wins
         lds[c] = v[i];                              // entries >= E pad with -inf
     }
@@ -361,8 +363,19 @@ __global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ lo
     const int wave = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    topk_any_wave(logits + (size_t)t * E, E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr,
-                  tk_lds[wave]);
+    // the logits come from an earlier launch: ordinary loads
+    double *lds = tk_lds[wave];
+    const double *lrow = logits + (size_t)t * E;
+    int32_t *ir = idx_out + (size_t)t * k;
+    float *wrw = w_out + (size_t)t * k;
+    if (E <= 64)
+        topk_rank_wave<1, false>(lrow, E, k, ir, wrw, nullptr, lds);
+    else if (E <= 128)
+        topk_rank_wave<2, false>(lrow, E, k, ir, wrw, nullptr, lds);
+    else if (E <= kRankMaxExperts)
+        topk_rank_wave<4, false>(lrow, E, k, ir, wrw, nullptr, lds);
+    else
+        topk_wave(lrow, E, k, ir, wrw, nullptr);
 }
 
 }  // namespace moe
