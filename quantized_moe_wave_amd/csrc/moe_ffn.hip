@@ -60,6 +60,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Workspace for up to cap tokens (S = cap * k slots).
 struct Workspace {
     double *logits = nullptr;     // [T][E]
+    double *lpart = nullptr;      // [kRlPartDoubles] partial logits of the split router
     int32_t *idx = nullptr;       // [T][k] (used when the caller passes no router_idx)
     float *w = nullptr;           // [T][k] (used when the caller passes no router_out)
     uint32_t *rcount = nullptr;   // [token groups] router completion counters (kept at zero)
@@ -218,6 +219,7 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
         return p;
     };
     w->logits = (double *)take(T * E * 8);
+    w->lpart = (double *)take((size_t)kRlPartDoubles * 8);
     w->idx = (int32_t *)take(S * 4);
     w->w = (float *)take(S * 4);
     w->rcount = (uint32_t *)take(T * 4);
@@ -409,9 +411,17 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     } else if (T <= 4) {
         launch_router<4, 1>(h, T, x, idx, wt, st);
     } else {
-        launch(pf, kStRouter, router_logits_kernel, dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp),
-               dim3(256), st, x, h->rw, h->rb, T, H, E, w.logits);
-        launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
+        // few token tiles: split H over more workgroups (partials summed in
+        // split order by the top-k kernel); ks*T*E stays below kRlPartDoubles
+        const int rtiles = ((T + kRlTok - 1) / kRlTok) * ((E + kRlExp - 1) / kRlExp);
+        int ks = 1;
+        if (E <= kRankMaxExperts)
+            while (ks < kRlMaxSplit && rtiles * ks < 128 && (H / 256) % (2 * ks) == 0) ks *= 2;
+        launch(pf, kStRouter, router_logits_kernel,
+               dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks), dim3(256), st, x, h->rw, h->rb, T, H,
+               E, w.logits, ks, w.lpart);
+        launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
+               w.lpart);
     }
 
     launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,

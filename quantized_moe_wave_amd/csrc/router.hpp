@@ -278,15 +278,24 @@ constexpr int kRlTok = 32, kRlExp = 32, kRlPf = 4;  // tile, and 16-column group
 
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
+// Split of H over blockIdx.z for small T: workgroup z covers columns
+// [z*H/ks, (z+1)*H/ks) and writes its partial sums to part[z][T][E] (the
+// bias in z = 0); topk_kernel adds the ks partials in z order. ks = 1 writes
+// the logits directly. H/ks must be a multiple of 256 (each wave's share a
+// whole number of kRlPf 16-column groups).
+constexpr int kRlMaxSplit = 16;
+constexpr int kRlPartDoubles = 256 * 1024;  // ks*T*E < 1024 * 256 for the ks the host picks
+
 __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x, const float *__restrict__ wr,
                                                             const float *__restrict__ bias, int T, int H, int E,
-                                                            double *__restrict__ logits) {
+                                                            double *__restrict__ logits, int ks,
+                                                            double *__restrict__ part_out) {
     __shared__ double part[4][2][2][4][64];  // [wave][token block][expert block][element][lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int t0 = blockIdx.x * kRlTok, e0 = blockIdx.y * kRlExp;
-    const int kq = H >> 2;                  // columns per wave (a multiple of 64)
-    const int kbeg = wave * kq;
+    const int kq = H / (4 * ks);            // columns per wave (a multiple of 64)
+    const int kbeg = blockIdx.z * (H / ks) + wave * kq;
     const int ngrp = kq >> 4;               // 16-column groups per wave
 
     // rows of this lane (clamped: rows past T or E load a valid row, never stored)
@@ -351,21 +360,46 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
         v += part[1][tb][eb][r][l];
         v += part[2][tb][eb][r][l];
         v += part[3][tb][eb][r][l];
-        if (t < T && e < E) logits[(size_t)t * E + e] = bias ? v + (double)bias[e] : v;
+        if (t < T && e < E) {
+            if (bias && blockIdx.z == 0) v += (double)bias[e];
+            if (ks == 1)
+                logits[(size_t)t * E + e] = v;
+            else
+                part_out[((size_t)blockIdx.z * T + t) * E + e] = v;
+        }
     }
 }
 
 // Top-k and renormalised weights of 4 tokens per workgroup, one wave each,
 // from logits written by the previous launch.
-__global__ __launch_bounds__(256) void topk_kernel(const double *__restrict__ logits, int T, int E, int k,
-                                                   int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+// One wave per token. ks > 1: the logits are first summed from the ks
+// partials of router_logits_kernel (z order) and written back to logits.
+__global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
+                                                   int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
+                                                   const double *__restrict__ part) {
     __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
-    const int wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) double sums[4][kRankMaxExperts];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    // the logits come from an earlier launch: ordinary loads
+    if (ks > 1) {  // E <= kRankMaxExperts here
+        for (int c = lane; c < E; c += 64) {
+            // all partials in flight together (index clamped), added in z order
+            double pv[kRlMaxSplit];
+#pragma unroll
+            for (int z = 0; z < kRlMaxSplit; ++z) pv[z] = part[((size_t)min(z, ks - 1) * T + t) * E + c];
+            double v = pv[0];
+#pragma unroll
+            for (int z = 1; z < kRlMaxSplit; ++z)
+                if (z < ks) v += pv[z];
+            sums[wave][c] = v;
+            logits[(size_t)t * E + c] = v;
+        }
+        lds_wave_sync();
+    }
+    // the logits come from an earlier launch (or this wave's sums): ordinary loads
     double *lds = tk_lds[wave];
-    const double *lrow = logits + (size_t)t * E;
+    const double *lrow = ks > 1 ? sums[wave] : logits + (size_t)t * E;
     int32_t *ir = idx_out + (size_t)t * k;
     float *wrw = w_out + (size_t)t * k;
     if (E <= 64)
