@@ -121,45 +121,47 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
 
 // Rank-based top-k of one token for a whole workgroup (E <= 256): the k
 // winners' experts and logits land in LDS at their slot. Same rule as the
-// other selections: larger logit first, equal logits to the lower index; NaN
-// counts as -inf. The logits are padded with -inf to 256 entries (a pad never
-// beats a real candidate: it is not larger, and on a tie its index is higher).
-// Candidate c's rank counts the logits that beat it, in fp64. Every lane of a
-// wave walks the same range of j, so each LDS read is a broadcast: for
-// E <= 128 candidate c = tid % 128 and waves 0-1 count j < 64, waves 2-3
-// j >= 64; for larger E candidate c = tid counts all 256.
+// other selections (rank_key: larger logit first, equal logits to the lower
+// index; NaN counts as -inf). The keys are padded with -inf keys to 256
+// entries (a pad never beats a real candidate: it is not larger, and on a tie
+// its index is higher). Candidate c's rank counts the keys above its own.
+// Every lane of a wave walks the same range of j, so each LDS read is a
+// broadcast: for E <= 128 candidate c = tid % 128 and waves 0-1 count j < 64,
+// waves 2-3 j >= 64; for larger E candidate c = tid counts all 256. The
+// thread that writes a winner is the one that loaded it (tid == c). lg: 256
+// LDS words of 8 bytes, which hold the keys.
 template <bool COHERENT>
 __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, double *lg, int *sel_e,
                                            double *sel_v) {
     __shared__ int rk_hi[128];
+    uint64_t *keys = (uint64_t *)lg;
     const int tid = threadIdx.x;
     const bool act = tid < 256;  // threads past 256 (larger workgroups) only join the barriers
+    double v = -INFINITY;
     if (act) {
         // COHERENT: written by other workgroups of this launch (agent-scope load)
         const int c = min(tid, E - 1);
-        const double v = COHERENT ? __hip_atomic_load(&lrow[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lrow[c];
-        lg[tid] = (tid < E && v == v) ? v : -INFINITY;
+        const double x = COHERENT ? __hip_atomic_load(&lrow[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lrow[c];
+        v = (tid < E && x == x) ? x : -INFINITY;
+        keys[tid] = rank_key(v, tid);
     }
     __syncthreads();
     const bool split = E <= 128;
     const int c = split ? (tid & 127) : (tid & 255);
     const int j0 = split ? ((tid >> 7) & 1) * 64 : 0;
     const int nj = act ? (split ? 64 : 256) : 0;
-    const double v = lg[c];
+    const uint64_t key = keys[c];
     int rank = 0;
     for (int jj = 0; jj < nj; jj += 8) {
-        double b[8];
+        uint64_t b[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const double2 p2 = *(const double2 *)&lg[j0 + jj + 2 * q];
+            const ulonglong2 p2 = *(const ulonglong2 *)&keys[j0 + jj + 2 * q];
             b[2 * q] = p2.x;
             b[2 * q + 1] = p2.y;
         }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int j = j0 + jj + q;
-            rank += (int)(b[q] > v) | ((int)(b[q] == v) & (int)(j < c));  // branch-free
-        }
+        for (int q = 0; q < 8; ++q) rank += (int)(b[q] > key);
     }
     if (act && split && tid >= 128) rk_hi[c] = rank;
     __syncthreads();

@@ -420,8 +420,11 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         launch(pf, kStRouter, router_logits_kernel,
                dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks), dim3(256), st, x, h->rw, h->rb, T, H,
                E, w.logits, ks, w.lpart);
-        launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
-               w.lpart);
+        if (E <= kRankMaxExperts)
+            launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
+                   w.lpart);
+        else
+            launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
     }
 
     launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,

@@ -26,48 +26,59 @@ constexpr int kRouterChunk = 256;  // hidden columns staged per step
 
 constexpr int kRankMaxExperts = 256;  // rank-based selection up to this many experts
 
+// Selection key of logit v of expert c < kRankMaxExperts: the fp64 bit pattern
+// mapped to an unsigned order (sign bit set for non-negative values, all bits
+// flipped for negative ones; -0 is first made +0), with its lowest 8 mantissa
+// bits replaced by 255 - c. Keys are distinct, and key order is logit order,
+// equal logits going to the lower index; logits whose gap is below 2^-44 of
+// their magnitude (far inside the near-tie band) are also ordered by index.
+// NaN must already be mapped to -inf. One 64-bit compare orders two keys.
+__device__ __forceinline__ uint64_t rank_key(double v, int c) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v + 0.0);
+    const uint64_t ord = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+    return (ord & ~0xFFull) | (uint64_t)(255 - c);
+}
+
 // One wave: top-k of one token's E <= kRankMaxExperts logits by rank. Each
-// candidate c counts the logits that beat it (larger, or equal with a lower
-// index); the k candidates with rank < k are the chosen experts and rank is
-// their slot. Same result as k rounds of argmax with the lower-index rule, in
-// fp64, without a serial chain of cross-lane steps. lds: this wave's scratch
-// of kRankMaxExperts + kMaxTopK doubles + kMaxTopK ints.
+// candidate c counts the keys (rank_key) above its own; the k candidates with
+// rank < k are the chosen experts and rank is their slot. Same result as k
+// rounds of argmax with the lower-index rule, without a serial chain of
+// cross-lane steps. lds: this wave's scratch of kRankMaxExperts + kMaxTopK
+// doubles + kMaxTopK ints.
 template <int PL, bool COHERENT = true>
 __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
                                                int *sidx, double *lds) {
     const int lane = threadIdx.x & 63;
+    uint64_t *keys = (uint64_t *)lds;
     double v[PL];
+    uint64_t key[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int c = lane + 64 * i;
         // COHERENT: the logits were written by other workgroups of this launch
         const double x = COHERENT ? __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                   : lrow[min(c, E - 1)];
-        v[i] = (c < E && x == x) ? x : -INFINITY;  // NaN never wins
-        lds[c] = v[i];                              // entries >= E pad with -inf
+        v[i] = (c < E && x == x) ? x : -INFINITY;  // NaN never wins; entries >= E pad with -inf
+        key[i] = rank_key(v[i], c);
+        keys[c] = key[i];
     }
     lds_wave_sync();
     int rank[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) rank[i] = 0;
-    // 16 logits per step, read as 8 broadcast 16-byte LDS loads issued together
+    // 16 keys per step, read as 8 broadcast 16-byte LDS loads issued together
     for (int j0 = 0; j0 < 64 * PL; j0 += 16) {
-        double a[16];
+        uint64_t a[16];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            const double2 p2 = *(const double2 *)&lds[j0 + 2 * q];
+            const ulonglong2 p2 = *(const ulonglong2 *)&keys[j0 + 2 * q];
             a[2 * q] = p2.x;
             a[2 * q + 1] = p2.y;
         }
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            const int j = j0 + q;
+        for (int q = 0; q < 16; ++q)
 #pragma unroll
-            for (int i = 0; i < PL; ++i) {
-                const int c = lane + 64 * i;
-                rank[i] += (int)(a[q] > v[i]) | ((int)(a[q] == v[i]) & (int)(j < c));  // branch-free
-            }
-        }
+            for (int i = 0; i < PL; ++i) rank[i] += (int)(a[q] > key[i]);
     }
     // winners into LDS (value and expert at their slot), global stores last
     double *sel = lds + kRankMaxExperts;
@@ -371,8 +382,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 }
 
 // Top-k and renormalised weights of 4 tokens per workgroup, one wave each,
-// from logits written by the previous launch.
-// One wave per token. ks > 1: the logits are first summed from the ks
+// from logits written by the previous launch (E <= kRankMaxExperts; larger E
+// takes topk_wide_kernel). ks > 1: the logits are first summed from the ks
 // partials of router_logits_kernel (z order) and written back to logits.
 __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
@@ -406,10 +417,17 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
         topk_rank_wave<1, false>(lrow, E, k, ir, wrw, nullptr, lds);
     else if (E <= 128)
         topk_rank_wave<2, false>(lrow, E, k, ir, wrw, nullptr, lds);
-    else if (E <= kRankMaxExperts)
-        topk_rank_wave<4, false>(lrow, E, k, ir, wrw, nullptr, lds);
     else
-        topk_wave(lrow, E, k, ir, wrw, nullptr);
+        topk_rank_wave<4, false>(lrow, E, k, ir, wrw, nullptr, lds);
+}
+
+// topk_kernel for E > kRankMaxExperts (k rounds of wave argmax; ks = 1): a
+// kernel of its own so that its registers do not weigh on the rank path.
+__global__ __launch_bounds__(256) void topk_wide_kernel(const double *__restrict__ logits, int T, int E, int k,
+                                                        int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    topk_wave(logits + (size_t)t * E, E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr);
 }
 
 }  // namespace moe
