@@ -139,35 +139,24 @@ __device__ __forceinline__ float silu_fast(float z) {
 // tiles[t] = (expert, first bucket slot, rows), t < *n_tiles. ngroups must be
 // a multiple of 4*CW; ncb = ngroups / (4*CW) column blocks; grid = 8 * ncb *
 // ceil(max tiles / 8). a_sinv holds 1/s of every row (nsb equal entries).
+// Main loop of one output tile (everything up to the epilogue). The LDS
+// buffers come in as separate restrict pointers, so the compiler knows which
+// global->LDS load each LDS read depends on and adds no wait of its own
+// beyond the fixed ones below (without that knowledge it drains every load in
+// flight before each header read).
 template <bool GATEUP, int RB, int CW, int NW>
-__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void expert_gemm_kernel(
-    const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
-    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
-    const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
+__device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_t *__restrict__ bqbuf,
+                                              uint8_t *__restrict__ hbuf, uint8_t *__restrict__ xsbuf,
+                                              float *__restrict__ svbuf, const uint8_t *__restrict__ W, int ngroups,
+                                              int nsb, const int32_t *__restrict__ entries, int k,
+                                              const f16 *__restrict__ a_hilo, const f16 *__restrict__ a_xs,
+                                              const float *__restrict__ a_sinv, int e, int r0, int rows, int rg0,
+                                              int wave, f32x4 (&X)[RB][CW], float (&fcur)[CW]) {
     using Sh = GemmShape<RB, CW, NW>;
-    constexpr int NT = 64 * NW;
     constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads;
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t *abuf = smem;
-    uint8_t *bqbuf = abuf + kGemmRing * Sh::ABuf;
-    uint8_t *hbuf = bqbuf + 2 * Sh::BqBuf;
-    uint8_t *xsbuf = hbuf + 2 * Sh::HdrBuf;
-    float *svbuf = (float *)(smem + Sh::SvOff);
-
-    const int ncb = ngroups / Sh::Groups;
-    const int ntl = *n_tiles;
-    const int per_xcd = (ntl + 7) >> 3;  // tiles per XCD (a contiguous range)
-    const int slot_id = blockIdx.x >> 3;
-    const int tile = (blockIdx.x & 7) * per_xcd + slot_id / ncb;
-    const int cblk = slot_id % ncb;
-    if (slot_id / ncb >= per_xcd || tile >= ntl) return;
-    const u32x4 tr = *(const u32x4 *)&tiles[tile];
-    const int e = (int)tr.x, r0 = (int)tr.y, rows = (int)tr.z;
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
     const int n = lane & 15, g = lane >> 4;
     const int K = nsb * kQ4Weights;
-    const int rg0 = cblk * Sh::Groups;
 
     // source row (token for GATEUP, bucket slot otherwise) of tile row r;
     // rows past the end of a partial tile repeat its last row
@@ -278,7 +267,6 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
         }
     };
 
-    f32x4 X[RB][CW];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -362,7 +350,6 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     //   q = 3, half 1: f = d_b / d_{b+1} (d_last after the last super-block)
     //   next q = 0, half 0: X *= f, tile by tile ahead of its MFMAs
     // A d of 0 counts as 1 (its scales are zeroed, only the min term is left).
-    float fcur[CW];
 #pragma unroll
     for (int cb = 0; cb < CW; ++cb) fcur[cb] = 1.f;
     auto min_term = [&](int b) {
@@ -490,6 +477,40 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW /
     for (int b = 0; b < nsb - 1; ++b) sb_step(b, std::integral_constant<bool, true>{});
     sb_step(nsb - 1, std::integral_constant<bool, false>{});
     wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
+}
+
+template <bool GATEUP, int RB, int CW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void expert_gemm_kernel(
+    const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
+    const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
+    const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
+    using Sh = GemmShape<RB, CW, NW>;
+    constexpr int NT = 64 * NW;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint8_t *abuf = smem;
+    uint8_t *bqbuf = abuf + kGemmRing * Sh::ABuf;
+    uint8_t *hbuf = bqbuf + 2 * Sh::BqBuf;
+    uint8_t *xsbuf = hbuf + 2 * Sh::HdrBuf;
+    float *svbuf = (float *)(smem + Sh::SvOff);
+
+    const int ncb = ngroups / Sh::Groups;
+    const int ntl = *n_tiles;
+    const int per_xcd = (ntl + 7) >> 3;  // tiles per XCD (a contiguous range)
+    const int slot_id = blockIdx.x >> 3;
+    const int tile = (blockIdx.x & 7) * per_xcd + slot_id / ncb;
+    const int cblk = slot_id % ncb;
+    if (slot_id / ncb >= per_xcd || tile >= ntl) return;
+    const u32x4 tr = *(const u32x4 *)&tiles[tile];
+    const int e = (int)tr.x, r0 = (int)tr.y, rows = (int)tr.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
+    const int n = lane & 15, g = lane >> 4;
+    const int rg0 = cblk * Sh::Groups;
+
+    f32x4 X[RB][CW];
+    float fcur[CW];
+    gemm_mainloop<GATEUP, RB, CW, NW>(abuf, bqbuf, hbuf, xsbuf, svbuf, W, ngroups, nsb, entries, k, a_hilo, a_xs,
+                                      a_sinv, e, r0, rows, rg0, wave, X, fcur);
 
     // results: X of tile rows rb*16 + 4g + i, columns of weight group
     // CW*wave + cb, times d of the last super-block and the row's 1/s; staged through LDS (once every wave

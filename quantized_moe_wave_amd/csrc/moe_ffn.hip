@@ -406,6 +406,7 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         h->last_T = T;
         return MOE_OK;
     }
+    bool staged_x = false;
     if (T == 1) {
         launch_router<1, 1>(h, T, x, idx, wt, st);
     } else if (T <= 4) {
@@ -420,18 +421,22 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         launch(pf, kStRouter, router_logits_kernel,
                dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks), dim3(256), st, x, h->rw, h->rb, T, H,
                E, w.logits, ks, w.lpart);
-        if (E <= kRankMaxExperts)
+        if (E <= kRankMaxExperts) {
+            // the top-k launch also stages x
             launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
-                   w.lpart);
-        else
+                   w.lpart, x, H, w.x_hilo, w.x_xs, w.x_sinv);
+            staged_x = true;
+        } else {
             launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
+        }
     }
 
     launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,
            w.tiles, w.big_tiles, w.n_tiles);
 
-    launch(pf, kStStageX, stage_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo, w.x_xs,
-           w.x_sinv);
+    if (!staged_x)
+        launch(pf, kStStageX, stage_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
+               w.x_xs, w.x_sinv);
 
     // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
     // (see gemm.hpp); 16-row x 256-column tiles (4 waves) for buckets of at

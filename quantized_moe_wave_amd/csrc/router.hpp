@@ -19,6 +19,7 @@
 // the softmax/top-k for that group's tokens, one wave per token.
 #pragma once
 #include "common.hpp"
+#include "stage.hpp"
 
 namespace moe {
 
@@ -385,14 +386,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 // from logits written by the previous launch (E <= kRankMaxExperts; larger E
 // takes topk_wide_kernel). ks > 1: the logits are first summed from the ks
 // partials of router_logits_kernel (z order) and written back to logits.
+// x non-null: the wave first stages its token's activation row (H columns)
+// for the grouped GEMM, as stage_kernel would (independent of the routing).
 __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
-                                                   const double *__restrict__ part) {
+                                                   const double *__restrict__ part, const float *__restrict__ x,
+                                                   int H, f16 *__restrict__ x_hilo, f16 *__restrict__ x_xs,
+                                                   float *__restrict__ x_sinv) {
     __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
     __shared__ __attribute__((aligned(16))) double sums[4][kRankMaxExperts];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
+    if (x) {
+        const int nh = H / kQ4Weights;
+        stage_row_wave(x + (size_t)t * H, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16,
+                       x_sinv + (size_t)t * nh);
+    }
     if (ks > 1) {  // E <= kRankMaxExperts here
         for (int c = lane; c < E; c += 64) {
             // all partials in flight together (index clamped), added in z order

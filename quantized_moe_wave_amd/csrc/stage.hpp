@@ -79,27 +79,98 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
     }
 }
 
-// One wave per row, one scale per row (the grouped GEMM applies the row's
-// 1/s once, after its last super-block): the row's largest magnitude sets s,
-// then every super-block is staged with it (same layout as stage_row_sb; the
-// per-super-block 1/s entries all hold the row's value).
+// One wave stages one row with one scale (the grouped GEMM applies the row's
+// 1/s once, after its last super-block; the per-super-block 1/s entries all
+// hold the row's value). The row's largest magnitude sets s. Same fragments,
+// rounding and sums as stage_row_sb, but all 64 lanes work: lanes 0-31 take
+// the even super-block of each pair, lanes 32-63 the odd one. Rows of up to
+// 2 * kStageRegPairs super-blocks are read once (every load issued before the
+// first use); longer rows are read twice.
+constexpr int kStageRegPairs = 8;
+__device__ __forceinline__ void stage_row_wave(const float *__restrict__ r, int nsb, f16 *__restrict__ hilo_row,
+                                               f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+    const int lane = threadIdx.x & 63;
+    const int f = lane & 31, s = f >> 2, g = f & 3, hb = lane >> 5;
+    const int off = s * 32 + g * 8;
+    const int npairs = (nsb + 1) >> 1;
+    const bool in_regs = npairs <= kStageRegPairs;
+    float4 va[kStageRegPairs], vb[kStageRegPairs];
+    float m = 0.f;
+    if (in_regs) {
+#pragma unroll
+        for (int p = 0; p < kStageRegPairs; ++p) {
+            if (p < npairs) {
+                const int b = min(2 * p + hb, nsb - 1);  // an odd tail repeats the last block (not stored)
+                va[p] = *(const float4 *)(r + b * kQ4Weights + off);
+                vb[p] = *(const float4 *)(r + b * kQ4Weights + off + 4);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < kStageRegPairs; ++p) {
+            if (p < npairs) {
+                const float4 a = va[p], c = vb[p];
+                m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                                   fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)))));
+            }
+        }
+    } else {
+        for (int c = lane * 4; c < nsb * kQ4Weights; c += 256) {
+            const float4 a = *(const float4 *)(r + c);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        }
+    }
+    const int se = stage_exponent(wave_max(m));
+    const float sc = ldexpf(1.f, se), sinv = ldexpf(1.f, -se);
+    auto emit = [&](int b, float4 a, float4 c) {
+        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+        f16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float y = v[perm8(e)] * sc;  // exact: power-of-two scaling
+            const f16 h = (f16)y;
+            hi[e] = h;
+            lo[e] = (f16)(y - (float)h);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part += v[i] * sc;
+        // sum of the 32 columns of k-step s: lanes 4s .. 4s+3 of this half
+        part += __shfl_xor(part, 1, kWave);
+        part += __shfl_xor(part, 2, kWave);
+        if (b < nsb) {
+            f16 *dst = hilo_row + (size_t)((b * 8 + s) * 4 + g) * 16;
+            *(f16x8 *)dst = hi;
+            *(f16x8 *)(dst + 8) = lo;
+            if (g == 0) {
+                const f16 h = (f16)part;
+                f16 *xd = xs_row + (size_t)b * 16;
+                xd[s] = h;
+                xd[8 + s] = (f16)(part - (float)h);
+            }
+            if (f == 0) sinv_row[b] = sinv;
+        }
+    };
+    if (in_regs) {
+#pragma unroll
+        for (int p = 0; p < kStageRegPairs; ++p)
+            if (p < npairs) emit(2 * p + hb, va[p], vb[p]);
+    } else {
+        for (int p = 0; p < npairs; ++p) {
+            const int b = 2 * p + hb, bl = min(b, nsb - 1);
+            emit(b, *(const float4 *)(r + bl * kQ4Weights + off), *(const float4 *)(r + bl * kQ4Weights + off + 4));
+        }
+    }
+}
+
+// One wave per row (stage_row_wave).
 __global__ __launch_bounds__(256) void stage_kernel(const float *__restrict__ src, int rows, int K, int ld_src,
                                                     f16 *__restrict__ hilo, f16 *__restrict__ xs,
                                                     float *__restrict__ sinv) {
     const int nsb = K / kQ4Weights;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
-    const int lane = threadIdx.x & 63;
-    const float *r = src + (size_t)row * ld_src;
-    float m = 0.f;
-    for (int c = lane * 4; c < K; c += 256) {
-        const float4 a = *(const float4 *)(r + c);
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-    }
-    const int se = stage_exponent(wave_max(m));
-    for (int b = 0; b < nsb; ++b)
-        stage_row_sb(r, nsb, b, hilo + (size_t)row * (2 * K), xs + (size_t)row * nsb * 16, sinv + (size_t)row * nsb,
-                     se);
+    stage_row_wave(src + (size_t)row * ld_src, nsb, hilo + (size_t)row * (2 * K), xs + (size_t)row * nsb * 16,
+                   sinv + (size_t)row * nsb);
 }
 
 }  // namespace moe
