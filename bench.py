@@ -220,15 +220,20 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
         T, k, H, I = wl.tokens, wl.top_k, wl.hidden, wl.inter
         if bound == "hbm":
             # decode: the gate/up kernel; routed gate+up weight bytes of each launch
+            # (T <= 4: the per-pair decode kernel, else the 16-row grouped GEMM)
             stage = "gate_up"
+            kname = "gateup_pair_kernel" if T <= 4 else "expert_gemm_kernel<gate_up, 16-row tiles>"
             prof = b.stage_times(steps, [stage])[stage]
             total_ms = sum(p[1] for p in prof)
             launches = sum(p[2] for p in prof)
+            if launches == 0 or total_ms <= 0:
+                raise RuntimeError(f"{wl.name}: no {stage} launches were timed")
             alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * nl for r, _, nl in prof)
             achieved = alg / (total_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gateup_pair_kernel"),
-                    "kernel": "gateup_pair_kernel (gate_up)", "avg_us": round(total_ms / launches * 1e3, 3),
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(kname) if T <= 4 else None,
+                    "kernel": f"{kname} ({stage})", "avg_us": round(total_ms / launches * 1e3, 3),
                     "algorithmic_bytes_per_launch": int(round(alg / launches))}
         else:
             # prefill: the gate/up grouped GEMM; 2 * rows * 2I * H flops per launch
@@ -236,6 +241,8 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
             prof = b.stage_times(steps, [stage])[stage]
             total_ms = sum(p[1] for p in prof)
             launches = sum(p[2] for p in prof)
+            if launches == 0 or total_ms <= 0:
+                raise RuntimeError(f"{wl.name}: no {stage} launches were timed")
             flops = sum(2.0 * stats[r][2] * 2 * I * H * nl for r, _, nl in prof)
             achieved = flops / (total_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
