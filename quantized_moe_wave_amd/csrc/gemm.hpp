@@ -249,12 +249,18 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             Al[rb] = *(const f16x8 *)(ab + r * kChunkBytes + jl * 16);
         }
     };
-    // the lane's 8 quant bytes of chunk c in each of its groups: half slot
-    // (c/2) % 2, bytes 8*(c%2) of the lane's 16
-    auto read_quants = [&](int c, u32x2 (&w)[CW]) {
-        const uint8_t *bq = bqbuf + ((c >> 1) & 1) * Sh::BqBuf + wave * CW * 1024;
+    // the lane's 16 quant bytes of half super-block hs (chunks 2hs, 2hs + 1:
+    // bytes 0-7 and 8-15) in each of its groups, from slot hs % 2; one
+    // 16-byte read per lane is free of bank conflicts, two 8-byte reads at a
+    // 16-byte stride are not
+    auto read_quants = [&](int hs, u32x4 (&w)[CW]) {
+        const uint8_t *bq = bqbuf + (hs & 1) * Sh::BqBuf + wave * CW * 1024;
 #pragma unroll
-        for (int cb = 0; cb < CW; ++cb) w[cb] = *(const u32x2 *)(bq + cb * 1024 + lane * 16 + (c & 1) * 8);
+        for (int cb = 0; cb < CW; ++cb) w[cb] = *(const u32x4 *)(bq + cb * 1024 + lane * 16);
+    };
+    auto quants_of = [&](const u32x4 (&w)[CW], bool odd, u32x2 (&o)[CW]) {
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) o[cb] = odd ? u32x2{w[cb].z, w[cb].w} : u32x2{w[cb].x, w[cb].y};
     };
     // B fragments of k-step 2q + s2: sub-block scale x quant (low nibbles for
     // s2 = 0, high for s2 = 1)
@@ -337,8 +343,10 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     Scales kc;
     f16x8 Ah0[RB], Al0[RB], B0[CW], Ah1[RB], Al1[RB], B1[CW];
     u32x2 wq[CW];
+    u32x4 wfull[CW];  // quants of the current half super-block
     read_scales(0, kc);
-    read_quants(0, wq);
+    read_quants(0, wfull);
+    quants_of(wfull, false, wq);
     read_a_half(0, 0, Ah0, Al0);
     build_b_half(0, 0, kc, wq, B0);
     __builtin_amdgcn_sched_barrier(0);
@@ -457,7 +465,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                     read_scales(b + 1, kc);
                     next_factor(b, !LOADS);
                 }
-                read_quants(c + 1, wn);
+                if ((q & 1) != 0) read_quants((c + 1) >> 1, wfull);  // chunk c+1 starts a half super-block
+                quants_of(wfull, ((q + 1) & 1) != 0, wn);
                 read_a_half(c + 1, 0, Ah0, Al0);
                 build_b_half((q + 1) & 3, 0, kc, wn, B0);
 #pragma unroll
