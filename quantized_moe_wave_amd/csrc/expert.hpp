@@ -92,9 +92,11 @@ __device__ __forceinline__ void q_times_scale_pair(uint32_t dA, uint32_t dB, f16
 
 // One k-step of the 8 bytes dA, dB (NIB 0: low nibbles, 1: high), as in
 // q_times_scale_pair.
+// a8, b8: dA >> 8 and dB >> 8, which the two nibble halves of the same bytes
+// can share.
 template <int NIB>
-__device__ __forceinline__ f16x8 q_times_scale_nib(uint32_t dA, uint32_t dB, f16 sc, const NibbleConsts &k) {
-    const uint32_t a8 = dA >> 8, b8 = dB >> 8;
+__device__ __forceinline__ f16x8 q_times_scale_nib(uint32_t dA, uint32_t dB, uint32_t a8, uint32_t b8, f16 sc,
+                                                   const NibbleConsts &k) {
     const uint32_t mask = NIB ? k.hi_mask : k.lo_mask, magic = NIB ? k.hi_magic : k.lo_magic;
     const f16x2 s2 = {sc, sc}, n2 = s2 * (f16)(NIB ? -64.f : -1024.f);
     const f16x2 r0 = __builtin_elementwise_fma(u32_as_f16x2((dA & mask) | magic), s2, n2);  // bytes 0, 2

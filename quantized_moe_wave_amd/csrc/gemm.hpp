@@ -258,18 +258,24 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) w[cb] = *(const u32x4 *)(bq + cb * 1024 + lane * 16);
     };
-    auto quants_of = [&](const u32x4 (&w)[CW], bool odd, u32x2 (&o)[CW]) {
+    // the chunk's 8 bytes and the same shifted right by 8 (shared by its two
+    // nibble halves)
+    auto quants_of = [&](const u32x4 (&w)[CW], bool odd, u32x4 (&o)[CW]) {
 #pragma unroll
-        for (int cb = 0; cb < CW; ++cb) o[cb] = odd ? u32x2{w[cb].z, w[cb].w} : u32x2{w[cb].x, w[cb].y};
+        for (int cb = 0; cb < CW; ++cb) {
+            const uint32_t a = odd ? w[cb].z : w[cb].x, b = odd ? w[cb].w : w[cb].y;
+            o[cb] = u32x4{a, b, a >> 8, b >> 8};
+        }
     };
     // B fragments of k-step 2q + s2: sub-block scale x quant (low nibbles for
     // s2 = 0, high for s2 = 1)
-    auto build_b_half = [&](int q, int s2, const Scales &kk, const u32x2 (&w)[CW], f16x8 (&Bf)[CW]) {
+    auto build_b_half = [&](int q, int s2, const Scales &kk, const u32x4 (&w)[CW], f16x8 (&Bf)[CW]) {
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
             const uint32_t scw = q < 2 ? kk.lo[cb] : kk.hi[cb];
             const f16 sc = (f16)(float)((scw >> (16 * (q & 1) + 8 * s2)) & 0xFFu);
-            Bf[cb] = s2 ? q_times_scale_nib<1>(w[cb].x, w[cb].y, sc, nk) : q_times_scale_nib<0>(w[cb].x, w[cb].y, sc, nk);
+            Bf[cb] = s2 ? q_times_scale_nib<1>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc, nk)
+                        : q_times_scale_nib<0>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc, nk);
         }
     };
 
@@ -342,7 +348,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 
     Scales kc;
     f16x8 Ah0[RB], Al0[RB], B0[CW], Ah1[RB], Al1[RB], B1[CW];
-    u32x2 wq[CW];
+    u32x4 wq[CW];
     u32x4 wfull[CW];  // quants of the current half super-block
     read_scales(0, kc);
     read_quants(0, wfull);
@@ -460,7 +466,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             // After the last chunk the fill reads stale but in-bounds LDS
             // and its results go unused.
             {
-                u32x2 wn[CW];
+                u32x4 wn[CW];
                 if (q == 3) {
                     read_scales(b + 1, kc);
                     next_factor(b, !LOADS);
