@@ -128,8 +128,9 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
                                  int32_t *entries, void *stream);
 
 /* Per-stage GPU timing for benchmarks. Stages of one forward, in launch order:
- * 0 router (logits, and for at most 4 tokens also the top-k), 1 topk, 2 bucket,
- * 3 stage_x, 4 gate_up (16-row tiles of buckets of at most 16 entries, or the
+ * 0 router (logits, and for at most 4 tokens also the top-k), 1 topk (which
+ * also stages x when num_experts <= 256), 2 bucket, 3 stage_x (when the top-k
+ * launch does not stage x), 4 gate_up (16-row tiles of buckets of at most 16 entries, or the
  * per-pair decode kernel), 5 gate_up_big (tiles of up to 64 rows for larger
  * buckets), 6 stage_h, 7 down (16-row tiles, or the fused decode down +
  * combine), 8 down_big, 9 combine; a stage a forward does not run has no
