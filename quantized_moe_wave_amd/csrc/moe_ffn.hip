@@ -423,8 +423,9 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
                E, w.logits, ks, w.lpart);
         if (E <= kRankMaxExperts) {
             // the top-k launch also stages x
-            launch(pf, kStTopk, topk_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
-                   w.lpart, x, H, w.x_hilo, w.x_xs, w.x_sinv);
+            auto topk = E <= 64 ? topk_kernel<1> : E <= 128 ? topk_kernel<2> : topk_kernel<4>;
+            launch(pf, kStTopk, topk, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks, w.lpart, x, H,
+                   w.x_hilo, w.x_xs, w.x_sinv);
             staged_x = true;
         } else {
             launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);

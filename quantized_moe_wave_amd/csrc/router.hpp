@@ -40,15 +40,42 @@ __device__ __forceinline__ uint64_t rank_key(double v, int c) {
     return (ord & ~0xFFull) | (uint64_t)(255 - c);
 }
 
-// One wave: top-k of one token's E <= kRankMaxExperts logits by rank. Each
-// candidate c counts the keys (rank_key) above its own; the k candidates with
-// rank < k are the chosen experts and rank is their slot. Same result as k
-// rounds of argmax with the lower-index rule, without a serial chain of
-// cross-lane steps. lds: this wave's scratch of kRankMaxExperts + kMaxTopK
-// doubles + kMaxTopK ints.
+// One wave: top-k of one token's E <= 64 * PL (<= kRankMaxExperts) logits by
+// rank. Each candidate c counts the keys (rank_key) above its own; the k
+// candidates with rank < k are the chosen experts and rank is their slot. Same
+// result as k rounds of argmax with the lower-index rule, without a serial
+// chain of cross-lane steps. lds: this wave's scratch of 64 * PL + kMaxTopK
+// doubles + kMaxTopK ints. Split in two: topk_rank_load (lane l's logits l,
+// l + 64, ...) and topk_rank_select (the rest), so that a caller can issue
+// other loads in between.
+template <int PL, bool COHERENT>
+__device__ __forceinline__ void topk_rank_load(const double *lrow, int E, double (&v)[PL]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int c = lane + 64 * i;
+        // COHERENT: the logits were written by other workgroups of this launch
+        v[i] = COHERENT ? __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                        : lrow[min(c, E - 1)];
+    }
+}
+
+template <int PL>
+__device__ __forceinline__ void topk_rank_select(const double (&lv)[PL], int E, int k, int32_t *idx_row,
+                                                 float *w_row, int *sidx, double *lds);
+
 template <int PL, bool COHERENT = true>
 __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k, int32_t *idx_row, float *w_row,
                                                int *sidx, double *lds) {
+    double v[PL];
+    topk_rank_load<PL, COHERENT>(lrow, E, v);
+    topk_rank_select<PL>(v, E, k, idx_row, w_row, sidx, lds);
+}
+
+// The selection of topk_rank_wave from the loaded logits.
+template <int PL>
+__device__ __forceinline__ void topk_rank_select(const double (&lv)[PL], int E, int k, int32_t *idx_row,
+                                                 float *w_row, int *sidx, double *lds) {
     const int lane = threadIdx.x & 63;
     uint64_t *keys = (uint64_t *)lds;
     double v[PL];
@@ -56,9 +83,7 @@ __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k,
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int c = lane + 64 * i;
-        // COHERENT: the logits were written by other workgroups of this launch
-        const double x = COHERENT ? __hip_atomic_load(&lrow[min(c, E - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                  : lrow[min(c, E - 1)];
+        const double x = lv[i];
         v[i] = (c < E && x == x) ? x : -INFINITY;  // NaN never wins; entries >= E pad with -inf
         key[i] = rank_key(v[i], c);
         keys[c] = key[i];
@@ -68,6 +93,8 @@ __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k,
 #pragma unroll
     for (int i = 0; i < PL; ++i) rank[i] = 0;
     // 16 keys per step, read as 8 broadcast 16-byte LDS loads issued together
+    // (two steps unrolled: a full unroll hoists every read into registers)
+#pragma unroll 2
     for (int j0 = 0; j0 < 64 * PL; j0 += 16) {
         uint64_t a[16];
 #pragma unroll
@@ -82,7 +109,7 @@ __device__ __forceinline__ void topk_rank_wave(const double *lrow, int E, int k,
             for (int i = 0; i < PL; ++i) rank[i] += (int)(a[q] > key[i]);
     }
     // winners into LDS (value and expert at their slot), global stores last
-    double *sel = lds + kRankMaxExperts;
+    double *sel = lds + 64 * PL;  // after the 64*PL keys
     int *sel_i = (int *)(sel + kMaxTopK);
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
@@ -383,27 +410,26 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 }
 
 // Top-k and renormalised weights of 4 tokens per workgroup, one wave each,
-// from logits written by the previous launch (E <= kRankMaxExperts; larger E
-// takes topk_wide_kernel). ks > 1: the logits are first summed from the ks
-// partials of router_logits_kernel (z order) and written back to logits.
-// x non-null: the wave first stages its token's activation row (H columns)
-// for the grouped GEMM, as stage_kernel would (independent of the routing).
+// from logits written by the previous launch; E <= 64 * PL (E <= kRankMaxExperts;
+// larger E takes topk_wide_kernel). ks > 1: the logits are first summed from
+// the ks partials of router_logits_kernel (z order) and written back to logits.
+// x non-null: the wave also stages its token's activation row (H columns) for
+// the grouped GEMM, as stage_kernel would (independent of the routing); the
+// row's loads are issued right after the logits' and land while the
+// selection runs.
+template <int PL>
 __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
                                                    const double *__restrict__ part, const float *__restrict__ x,
                                                    int H, f16 *__restrict__ x_hilo, f16 *__restrict__ x_xs,
                                                    float *__restrict__ x_sinv) {
-    __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
-    __shared__ __attribute__((aligned(16))) double sums[4][kRankMaxExperts];
+    __shared__ __attribute__((aligned(16))) double tk_lds[4][64 * PL + kMaxTopK + kMaxTopK / 2];
+    __shared__ __attribute__((aligned(16))) double sums[4][64 * PL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
-    if (x) {
-        const int nh = H / kQ4Weights;
-        stage_row_wave(x + (size_t)t * H, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16,
-                       x_sinv + (size_t)t * nh);
-    }
-    if (ks > 1) {  // E <= kRankMaxExperts here
+    const double *lrow = logits + (size_t)t * E;
+    if (ks > 1) {
         for (int c = lane; c < E; c += 64) {
             // all partials in flight together (index clamped), added in z order
             double pv[kRlMaxSplit];
@@ -417,18 +443,20 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
             logits[(size_t)t * E + c] = v;
         }
         lds_wave_sync();
+        lrow = sums[wave];
     }
-    // the logits come from an earlier launch (or this wave's sums): ordinary loads
-    double *lds = tk_lds[wave];
-    const double *lrow = ks > 1 ? sums[wave] : logits + (size_t)t * E;
-    int32_t *ir = idx_out + (size_t)t * k;
-    float *wrw = w_out + (size_t)t * k;
-    if (E <= 64)
-        topk_rank_wave<1, false>(lrow, E, k, ir, wrw, nullptr, lds);
-    else if (E <= 128)
-        topk_rank_wave<2, false>(lrow, E, k, ir, wrw, nullptr, lds);
-    else
-        topk_rank_wave<4, false>(lrow, E, k, ir, wrw, nullptr, lds);
+    double lv[PL];
+    topk_rank_load<PL, false>(lrow, E, lv);
+    const int nh = H / kQ4Weights;
+    const bool row_in_regs = x && (nh + 1) / 2 <= kStageRegPairs;
+    StagedRow sr;
+    if (row_in_regs) stage_row_load(x + (size_t)t * H, nh, sr);
+    topk_rank_select<PL>(lv, E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, tk_lds[wave]);
+    if (row_in_regs)
+        stage_row_store(sr, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16, x_sinv + (size_t)t * nh);
+    else if (x)
+        stage_row_wave(x + (size_t)t * H, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16,
+                       x_sinv + (size_t)t * nh);
 }
 
 // topk_kernel for E > kRankMaxExperts (k rounds of wave argmax; ks = 1): a

@@ -79,86 +79,119 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
     }
 }
 
-// One wave stages one row with one scale (the grouped GEMM applies the row's
-// 1/s once, after its last super-block; the per-super-block 1/s entries all
-// hold the row's value). The row's largest magnitude sets s. Same fragments,
-// rounding and sums as stage_row_sb, but all 64 lanes work: lanes 0-31 take
-// the even super-block of each pair, lanes 32-63 the odd one. Rows of up to
-// 2 * kStageRegPairs super-blocks are read once (every load issued before the
-// first use); longer rows are read twice.
+// Staging of a whole row with one scale, by one wave (the grouped GEMM
+// applies the row's 1/s once, after its last super-block; the
+// per-super-block 1/s entries all hold the row's value). The row's largest
+// magnitude sets s. Same fragments, rounding and sums as stage_row_sb, but
+// all 64 lanes work: lanes 0-31 take the even super-block of each pair, lanes
+// 32-63 the odd one. Rows of up to 2 * kStageRegPairs super-blocks are read
+// once (every load issued before the first use); longer rows are read twice.
 constexpr int kStageRegPairs = 8;
-__device__ __forceinline__ void stage_row_wave(const float *__restrict__ r, int nsb, f16 *__restrict__ hilo_row,
-                                               f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
-    const int lane = threadIdx.x & 63;
-    const int f = lane & 31, s = f >> 2, g = f & 3, hb = lane >> 5;
-    const int off = s * 32 + g * 8;
-    const int npairs = (nsb + 1) >> 1;
-    const bool in_regs = npairs <= kStageRegPairs;
+
+// A row of at most 2 * kStageRegPairs super-blocks in registers: pair p holds
+// super-block 2p (lanes 0-31) and 2p + 1 (lanes 32-63), 8 columns per lane.
+struct StagedRow {
     float4 va[kStageRegPairs], vb[kStageRegPairs];
+};
+
+// Issue the loads of a row into sr (no wait: the caller may do other work
+// while they are in flight). Requires (nsb + 1) / 2 <= kStageRegPairs.
+__device__ __forceinline__ void stage_row_load(const float *__restrict__ r, int nsb, StagedRow &sr) {
+    const int lane = threadIdx.x & 63;
+    const int f = lane & 31, hb = lane >> 5;
+    const int off = (f >> 2) * 32 + (f & 3) * 8;
+    const int npairs = (nsb + 1) >> 1;
+#pragma unroll
+    for (int p = 0; p < kStageRegPairs; ++p) {
+        if (p < npairs) {
+            const int b = min(2 * p + hb, nsb - 1);  // an odd tail repeats the last block (not stored)
+            sr.va[p] = *(const float4 *)(r + b * kQ4Weights + off);
+            sr.vb[p] = *(const float4 *)(r + b * kQ4Weights + off + 4);
+        }
+    }
+}
+
+// The 8 columns (a, c) of super-block b owned by this lane, scaled by sc:
+// fp16 hi/lo in fragment order, the k-step's 32-column sum (over the 4 lanes
+// of the k-step), and 1/s. All lanes must call it together.
+__device__ __forceinline__ void stage_emit(int b, float4 a, float4 c, float sc, float sinv, int nsb,
+                                           f16 *__restrict__ hilo_row, f16 *__restrict__ xs_row,
+                                           float *__restrict__ sinv_row) {
+    const int f = threadIdx.x & 31, s = f >> 2, g = f & 3;
+    const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+    f16x8 hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float y = v[perm8(e)] * sc;  // exact: power-of-two scaling
+        const f16 h = (f16)y;
+        hi[e] = h;
+        lo[e] = (f16)(y - (float)h);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part += v[i] * sc;
+    // sum of the 32 columns of k-step s: lanes 4s .. 4s+3 of this half
+    part += __shfl_xor(part, 1, kWave);
+    part += __shfl_xor(part, 2, kWave);
+    if (b < nsb) {
+        f16 *dst = hilo_row + (size_t)((b * 8 + s) * 4 + g) * 16;
+        *(f16x8 *)dst = hi;
+        *(f16x8 *)(dst + 8) = lo;
+        if (g == 0) {
+            const f16 h = (f16)part;
+            f16 *xd = xs_row + (size_t)b * 16;
+            xd[s] = h;
+            xd[8 + s] = (f16)(part - (float)h);
+        }
+        if (f == 0) sinv_row[b] = sinv;
+    }
+}
+
+// Scale and store a row loaded by stage_row_load.
+__device__ __forceinline__ void stage_row_store(const StagedRow &sr, int nsb, f16 *__restrict__ hilo_row,
+                                                f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+    const int hb = (threadIdx.x & 63) >> 5;
+    const int npairs = (nsb + 1) >> 1;
     float m = 0.f;
-    if (in_regs) {
 #pragma unroll
-        for (int p = 0; p < kStageRegPairs; ++p) {
-            if (p < npairs) {
-                const int b = min(2 * p + hb, nsb - 1);  // an odd tail repeats the last block (not stored)
-                va[p] = *(const float4 *)(r + b * kQ4Weights + off);
-                vb[p] = *(const float4 *)(r + b * kQ4Weights + off + 4);
-            }
-        }
-#pragma unroll
-        for (int p = 0; p < kStageRegPairs; ++p) {
-            if (p < npairs) {
-                const float4 a = va[p], c = vb[p];
-                m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                                   fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)))));
-            }
-        }
-    } else {
-        for (int c = lane * 4; c < nsb * kQ4Weights; c += 256) {
-            const float4 a = *(const float4 *)(r + c);
-            m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    for (int p = 0; p < kStageRegPairs; ++p) {
+        if (p < npairs) {
+            const float4 a = sr.va[p], c = sr.vb[p];
+            m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                               fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)))));
         }
     }
     const int se = stage_exponent(wave_max(m));
     const float sc = ldexpf(1.f, se), sinv = ldexpf(1.f, -se);
-    auto emit = [&](int b, float4 a, float4 c) {
-        const float v[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
-        f16x8 hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float y = v[perm8(e)] * sc;  // exact: power-of-two scaling
-            const f16 h = (f16)y;
-            hi[e] = h;
-            lo[e] = (f16)(y - (float)h);
-        }
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part += v[i] * sc;
-        // sum of the 32 columns of k-step s: lanes 4s .. 4s+3 of this half
-        part += __shfl_xor(part, 1, kWave);
-        part += __shfl_xor(part, 2, kWave);
-        if (b < nsb) {
-            f16 *dst = hilo_row + (size_t)((b * 8 + s) * 4 + g) * 16;
-            *(f16x8 *)dst = hi;
-            *(f16x8 *)(dst + 8) = lo;
-            if (g == 0) {
-                const f16 h = (f16)part;
-                f16 *xd = xs_row + (size_t)b * 16;
-                xd[s] = h;
-                xd[8 + s] = (f16)(part - (float)h);
-            }
-            if (f == 0) sinv_row[b] = sinv;
-        }
-    };
-    if (in_regs) {
-#pragma unroll
-        for (int p = 0; p < kStageRegPairs; ++p)
-            if (p < npairs) emit(2 * p + hb, va[p], vb[p]);
-    } else {
-        for (int p = 0; p < npairs; ++p) {
-            const int b = 2 * p + hb, bl = min(b, nsb - 1);
-            emit(b, *(const float4 *)(r + bl * kQ4Weights + off), *(const float4 *)(r + bl * kQ4Weights + off + 4));
-        }
+    for (int p = 0; p < kStageRegPairs; ++p)
+        if (p < npairs) stage_emit(2 * p + hb, sr.va[p], sr.vb[p], sc, sinv, nsb, hilo_row, xs_row, sinv_row);
+}
+
+// Load, scale and store one row (one wave).
+__device__ __forceinline__ void stage_row_wave(const float *__restrict__ r, int nsb, f16 *__restrict__ hilo_row,
+                                               f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+    const int npairs = (nsb + 1) >> 1;
+    if (npairs <= kStageRegPairs) {
+        StagedRow sr;
+        stage_row_load(r, nsb, sr);
+        stage_row_store(sr, nsb, hilo_row, xs_row, sinv_row);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int f = lane & 31, hb = lane >> 5;
+    const int off = (f >> 2) * 32 + (f & 3) * 8;
+    float m = 0.f;
+    for (int c = lane * 4; c < nsb * kQ4Weights; c += 256) {
+        const float4 a = *(const float4 *)(r + c);
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    }
+    const int se = stage_exponent(wave_max(m));
+    const float sc = ldexpf(1.f, se), sinv = ldexpf(1.f, -se);
+    for (int p = 0; p < npairs; ++p) {
+        const int b = 2 * p + hb, bl = min(b, nsb - 1);
+        stage_emit(b, *(const float4 *)(r + bl * kQ4Weights + off), *(const float4 *)(r + bl * kQ4Weights + off + 4),
+                   sc, sinv, nsb, hilo_row, xs_row, sinv_row);
     }
 }
 
