@@ -229,6 +229,24 @@ def test_many_experts(T):
     layer.close()
 
 
+@pytest.mark.parametrize("E,T", [(256, 3), (256, 40), (160, 40)])
+def test_experts_up_to_256(E, T):
+    """128 < E <= 256: the widest rank selection (every candidate counts 256
+    keys; E = 256 uses the whole 8-bit index field of the key), on the decode
+    path (T = 3) and the general path (T = 40)."""
+    print(f"[parity] E={E} k=8 T={T}", flush=True)
+    import dataclasses
+
+    import synth as _s
+
+    wl = dataclasses.replace(_s.WORKLOADS["tiny"], name=f"e{E}", experts=E, top_k=8)
+    inp = _s.make_inputs(wl, seed=40 + E)
+    layer, dev = parity.make_layer(inp)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=50 + T))
+    parity.check_parity(inp2, g)
+    layer.close()
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 300), ("30b-batch", 300)])
 def test_big_tiles_full_parity(name, T):
     """A bias that sends every token to expert 0 makes 128-row grouped-GEMM
