@@ -414,13 +414,21 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     } else {
         // few token tiles: split H over more workgroups (partials summed in
         // split order by the top-k kernel); ks*T*E stays below kRlPartDoubles
+        // many token tiles: 8 waves per workgroup (two per SIMD) where each
+        // wave's share of H is whole 64-column groups; few: 4 waves, and the
+        // split over workgroups below supplies the parallelism
         const int rtiles = ((T + kRlTok - 1) / kRlTok) * ((E + kRlExp - 1) / kRlExp);
+        const int nwv = H % 512 == 0 && rtiles >= 128 ? 8 : 4;
         int ks = 1;
         if (E <= kRankMaxExperts)
-            while (ks < kRlMaxSplit && rtiles * ks < 128 && (H / 256) % (2 * ks) == 0) ks *= 2;
-        launch(pf, kStRouter, router_logits_kernel,
-               dim3((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks), dim3(256), st, x, h->rw, h->rb, T, H,
-               E, w.logits, ks, w.lpart);
+            while (ks < kRlMaxSplit && rtiles * ks < 128 && (H / (64 * nwv)) % (2 * ks) == 0) ks *= 2;
+        const dim3 rgrid((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks);
+        if (nwv == 8)
+            launch(pf, kStRouter, router_logits_kernel<8>, rgrid, dim3(512), st, x, h->rw, h->rb, T, H, E, w.logits,
+                   ks, w.lpart);
+        else
+            launch(pf, kStRouter, router_logits_kernel<4>, rgrid, dim3(256), st, x, h->rw, h->rb, T, H, E, w.logits,
+                   ks, w.lpart);
         if (E <= kRankMaxExperts) {
             // the top-k launch also stages x
             auto topk = E <= 64 ? topk_kernel<1> : E <= 128 ? topk_kernel<2> : topk_kernel<4>;

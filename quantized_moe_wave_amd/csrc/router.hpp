@@ -302,10 +302,11 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
 // an fp64 sum of exact products (as in the plain definition) up to summation
 // order.
 //
-// Workgroup tile: 32 tokens x 32 experts, 4 waves; wave w sums the hidden
-// columns [w*H/4, (w+1)*H/4) into 2 x 2 MFMA tiles (16 tokens x 16 experts
-// each), and the 4 partial tiles are added in wave order through LDS (a fixed
-// order: results are reproducible).
+// Workgroup tile: 32 tokens x 32 experts, NWV waves (8 where H allows, so
+// that two waves share each SIMD and hide each other's load and MFMA
+// latency); wave w sums the hidden columns [w*H/NWV, (w+1)*H/NWV) into 2 x 2
+// MFMA tiles (16 tokens x 16 experts each), and the NWV partial tiles are
+// added in wave order through LDS (a fixed order: results are reproducible).
 // Column pairing: for 16 consecutive columns from k0, lane l (n = l%16,
 // g = l/16) loads the 4 floats at k0 + 4g of its token row (A) and of its
 // expert row (B); MFMA step i (0..3) uses element i, so lane group g covers
@@ -320,20 +321,22 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 // Split of H over blockIdx.z for small T: workgroup z covers columns
 // [z*H/ks, (z+1)*H/ks) and writes its partial sums to part[z][T][E] (the
 // bias in z = 0); topk_kernel adds the ks partials in z order. ks = 1 writes
-// the logits directly. H/ks must be a multiple of 256 (each wave's share a
-// whole number of kRlPf 16-column groups).
+// the logits directly. H/ks must be a multiple of 64 * NWV (each wave's share
+// a whole number of kRlPf 16-column groups).
 constexpr int kRlMaxSplit = 16;
 constexpr int kRlPartDoubles = 256 * 1024;  // ks*T*E < 1024 * 256 for the ks the host picks
 
-__global__ __launch_bounds__(256) void router_logits_kernel(const float *__restrict__ x, const float *__restrict__ wr,
-                                                            const float *__restrict__ bias, int T, int H, int E,
-                                                            double *__restrict__ logits, int ks,
-                                                            double *__restrict__ part_out) {
-    __shared__ double part[4][2][2][4][64];  // [wave][token block][expert block][element][lane]
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void router_logits_kernel(const float *__restrict__ x,
+                                                                 const float *__restrict__ wr,
+                                                                 const float *__restrict__ bias, int T, int H, int E,
+                                                                 double *__restrict__ logits, int ks,
+                                                                 double *__restrict__ part_out) {
+    __shared__ double part[NWV][2][2][4][64];  // [wave][token block][expert block][element][lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int t0 = blockIdx.x * kRlTok, e0 = blockIdx.y * kRlExp;
-    const int kq = H / (4 * ks);            // columns per wave (a multiple of 64)
+    const int kq = H / (NWV * ks);          // columns per wave (a multiple of 64)
     const int kbeg = blockIdx.z * (H / ks) + wave * kq;
     const int ngrp = kq >> 4;               // 16-column groups per wave
 
@@ -389,16 +392,15 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const float *__restr
 #pragma unroll
             for (int r = 0; r < 4; ++r) part[wave][tb][eb][r][lane] = acc[tb][eb][r];
     __syncthreads();
-    // 1024 outputs, 4 per thread: combo c = (tb, eb, r, lane)
+    // 1024 outputs, 1024 / (64 NWV) per thread: combo c = (tb, eb, r, lane)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = threadIdx.x + 256 * q;
+    for (int q = 0; q < 1024 / (64 * NWV); ++q) {
+        const int c = threadIdx.x + 64 * NWV * q;
         const int l = c & 63, r = (c >> 6) & 3, eb = (c >> 8) & 1, tb = c >> 9;
         const int t = t0 + 16 * tb + (l >> 4) + 4 * r, e = e0 + 16 * eb + (l & 15);
         double v = part[0][tb][eb][r][l];
-        v += part[1][tb][eb][r][l];
-        v += part[2][tb][eb][r][l];
-        v += part[3][tb][eb][r][l];
+#pragma unroll
+        for (int w = 1; w < NWV; ++w) v += part[w][tb][eb][r][l];
         if (t < T && e < E) {
             if (bias && blockIdx.z == 0) v += (double)bias[e];
             if (ks == 1)
