@@ -2,7 +2,7 @@
 //
 //   router_small_kernel       router logits (fp64) and x staging
 //   gateup_pair_kernel        one (token, slot) pair x one 16-row weight group
-//                             per workgroup, the four waves splitting the
+//                             per workgroup, its waves splitting the
 //                             reduction dimension; the workgroup finds the
 //                             pair's expert itself (top-k of its token)
 //   down_combine_small_kernel down projection of one token's k experts fused
@@ -12,7 +12,7 @@
 //                             layout)
 //
 // Every workgroup recomputing its token's top-k from the logits (a few
-// hundred fp64 compares per thread) is cheaper at decode than handing the
+// hundred 64-bit key compares per thread) is cheaper at decode than handing the
 // choice between workgroups, which costs several dependent memory round trips.
 //
 // Same arithmetic as the general path (router.hpp, stage.hpp, expert.hpp); the
@@ -294,11 +294,14 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
     for (int i = 0; i < 4; ++i) acc[i] += sv[i] * (dd * P[i] - dmin * Q[i]);
 }
 
-// Grid (T*k pairs, I/8 row groups), 256 threads. Pair p = t*k + j: the
+// Grid (T*k pairs, I/8 row groups), kGpWaves waves. Pair p = t*k + j: the
 // workgroup stages token t's A row in LDS and computes the 8 gate + 8 up rows
-// of row group rg of expert idx[p] for that single row (MFMA row 0), the four
-// waves splitting the super-blocks. Output h[p][I] = SiLU(gate) * up.
-__global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restrict__ GU, int ngroups, int nsb,
+// of row group rg of expert idx[p] for that single row (MFMA row 0), the waves
+// splitting the super-blocks (one each at H = 2048, so that each wave's chain
+// of dependent MFMAs is one super-block long). Output h[p][I] = SiLU(gate) * up.
+constexpr int kGpWaves = 8;
+
+__global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_t *__restrict__ GU, int ngroups, int nsb,
                                                           const double *__restrict__ logits, int E, int k,
                                                           const f16 *__restrict__ x_hilo, const f16 *__restrict__ x_xs,
                                                           const float *__restrict__ x_sinv, float *__restrict__ h,
@@ -306,7 +309,7 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
     __shared__ __attribute__((aligned(16))) f16 arow[2 * kSmallMaxH];
     __shared__ __attribute__((aligned(16))) f16 axs[kSmallMaxH / kQ4Weights * 16];
     __shared__ float asv[kSmallMaxH / kQ4Weights];
-    __shared__ f32x4 red[4][64];
+    __shared__ f32x4 red[kGpWaves][64];
     __shared__ __attribute__((aligned(16))) double lg[kRankMaxExperts];
     __shared__ int sel_e[kMaxTopK];
     __shared__ double sel_v[kMaxTopK];
@@ -317,11 +320,12 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
 
     // token t's staged row: loaded into registers first, so that these loads
     // and the top-k's logit loads are in flight together; stored to LDS after
-    constexpr int kRowLoads = kSmallMaxH / 4 / 256;  // 16-byte pieces per thread
+    constexpr int NT = kGpWaves * 64;
+    constexpr int kRowLoads = kSmallMaxH / 4 / NT;  // 16-byte pieces per thread
     u32x4 xr[kRowLoads];
     const u32x4 *xsrc = (const u32x4 *)(x_hilo + (size_t)t * 2 * H);
 #pragma unroll
-    for (int i = 0; i < kRowLoads; ++i) xr[i] = xsrc[min(tid + 256 * i, H / 4 - 1)];
+    for (int i = 0; i < kRowLoads; ++i) xr[i] = xsrc[min(tid + NT * i, H / 4 - 1)];
     const u32x2 xsr = ((const u32x2 *)(x_xs + (size_t)t * nsb * 16))[min(tid, nsb * 4 - 1)];
     const float svr = x_sinv[(size_t)t * nsb + min(tid, nsb - 1)];
     // expert of pair p = t*k + j: slot j of token t's top-k
@@ -329,17 +333,17 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
     const int e = sel_e[p - t * k];
 #pragma unroll
     for (int i = 0; i < kRowLoads; ++i)
-        if (tid + 256 * i < H / 4) ((u32x4 *)arow)[tid + 256 * i] = xr[i];
+        if (tid + NT * i < H / 4) ((u32x4 *)arow)[tid + NT * i] = xr[i];
     if (tid < nsb * 4) ((u32x2 *)axs)[tid] = xsr;
     if (tid < nsb) asv[tid] = svr;
     __syncthreads();
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
 
-    // wave w takes super-blocks w, w+4, ...; two per pass
+    // wave w takes super-blocks w, w + kGpWaves, ...; two per pass
     auto load_pass = [&](int b0, u32x4 (&q0)[2], u32x4 (&q1)[2], u32x4 (&hd)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint8_t *blk = wg + (size_t)min(b0 + 4 * i, nsb - 1) * kGroupSbBytes;
+            const uint8_t *blk = wg + (size_t)min(b0 + kGpWaves * i, nsb - 1) * kGroupSbBytes;
             q0[i] = *(const u32x4 *)(blk + lane * 16);
             q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
             hd[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
@@ -350,11 +354,11 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const bool a_ok = (n == 0);  // the tile's only row
-    for (int b0 = wave; b0 < nsb; b0 += 8) {
+    for (int b0 = wave; b0 < nsb; b0 += 2 * kGpWaves) {
         if (b0 != wave) load_pass(b0, q0, q1, hd);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int b = b0 + 4 * i;
+            const int b = b0 + kGpWaves * i;
             if (b < nsb) {
                 auto afrag = [&](int s, f16x8 &hi, f16x8 &lo) {
                     const f16 *ap = &arow[((b * 8 + s) * 4 + g) * 16];
@@ -372,13 +376,15 @@ __global__ __launch_bounds__(256) void gateup_pair_kernel(const uint8_t *__restr
     red[wave][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
-    const float r = red[0][lane][0] + red[1][lane][0] + red[2][lane][0] + red[3][lane][0];
+    float r = red[0][lane][0];
+#pragma unroll
+    for (int w = 1; w < kGpWaves; ++w) r += red[w][lane][0];
     const float u = __shfl_xor(r, 8, kWave);
     if (lane < 8) h[(size_t)p * I + rg * 8 + lane] = silu_f(r) * u;
 }
 
-constexpr int kDcWaves = 8;        // waves per down/combine workgroup
-constexpr int kDcMaxUnits = 4;     // (slot, super-block) units a wave holds in flight
+constexpr int kDcWaves = 12;       // waves per down/combine workgroup
+constexpr int kDcMaxUnits = 2;     // (slot, super-block) units a wave holds in flight
 
 // Grid (H/16 row groups + 1, T tokens), 512 threads. The k*nsb (slot j,
 // super-block b) units of one token are spread over the waves; each unit

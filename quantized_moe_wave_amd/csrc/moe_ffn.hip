@@ -397,7 +397,7 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         // decode path: three launches (see decode.hpp)
         launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
                w.logits, w.x_hilo, w.x_xs, w.x_sinv);
-        launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(256), st, h->gu, I / 8, nh, w.logits, E, k,
+        launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
         launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
                H / kRowGroup, ni, w.logits, E, T, k, w.h, I, out, H, idx, wt, w.counts, w.offsets, w.entries, w.pos);
