@@ -16,6 +16,8 @@ steps with events stamped at its own start and end (hipExtLaunchKernelGGL);
 its roofline fraction uses algorithmic bytes (decode: routed gate+up Q4_K
 weight bytes) or flops (prefill: 2*T*k*2*H*I) per launch.
 
+The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
+
 The CPU baseline is the fp64 oracle as it stands, timed on this host on a
 bounded sample of the same workload.
 
@@ -53,6 +55,9 @@ def parse_args():
     ap.add_argument("--prefill-workload", default="30b-prefill")
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--extra-workloads", default="30b-batch,235b-shape",
+                    help="comma-separated workloads whose whole-step time is reported under \"others\" ('' for none)")
+    ap.add_argument("--extra-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--stages", action="store_true", help="also time every stage (eager pass, to stderr)")
@@ -267,6 +272,41 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
         raise
 
 
+def measure_step(wl, steps: int, eager: bool, want_stages: bool = False) -> dict:
+    """Whole-step time of one more workload: tokens/s and the step's routed-expert bytes and algorithmic flops
+    against the HBM and MFMA peaks."""
+    import torch
+
+    b = Bench(wl, replicas_for(wl))
+    try:
+        stats = b.routing()
+        ms = b.timed(steps, max(3, steps // 10), eager)
+        if want_stages:
+            import quantized_moe_wave_amd as q
+
+            for st, lst in b.stage_times(steps, q.moe_ffn_stage_names()).items():
+                n = sum(p[2] for p in lst)
+                if n:
+                    log(f"{wl.name}: stage {st:12s} {sum(p[1] for p in lst) / n * 1e3:9.2f} us avg over {n} launches")
+    finally:
+        b.close()
+        del b
+        torch.cuda.empty_cache()
+    log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps; routing per replica {stats}")
+    U = sum(st[0] for st in stats) / len(stats)
+    T, k, H, I, E = wl.tokens, wl.top_k, wl.hidden, wl.inter, wl.experts
+    step_bytes = U * wl.expert_bytes
+    flops = 2.0 * T * k * 3 * H * I + 2.0 * T * E * H
+    sec = ms * 1e-3
+    return {"workload": wl.name, "tokens": T, "steps": steps, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(T / sec, 1), "distinct_experts": U,
+            "max_tokens_per_expert": max(st[1] for st in stats),
+            "hbm_step": {"routed_expert_bytes": int(step_bytes), "achieved_gbs": round(step_bytes / sec / 1e9, 1),
+                         "frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4)},
+            "mfma_step": {"algorithmic_tflops": round(flops / sec / 1e12, 2),
+                          "frac": round(flops / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
+
+
 def cpu_baseline(inp, seconds: float):
     """The oracle on T=1 forwards of replica 0's weights, one token per call, for ~seconds."""
     import numpy as np
@@ -366,6 +406,9 @@ def main() -> int:
             "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
             "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof,
         }
+    extras = [w for w in args.extra_workloads.split(",") if w]
+    if extras:
+        line["others"] = [measure_step(synth.WORKLOADS[w], args.extra_steps, args.eager, args.stages) for w in extras]
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {wl.name} for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(host0, args.cpu_seconds)
