@@ -6,14 +6,16 @@
 //                             reduction dimension; the workgroup finds the
 //                             pair's expert itself (top-k of its token)
 //   down_combine_small_kernel down projection of one token's k experts fused
-//                             with the router-weighted sum (slot order), again
-//                             with its own top-k; one extra workgroup writes
-//                             the routing outputs (indices, weights, bucket
-//                             layout)
+//                             with the router-weighted sum (slot order), the
+//                             experts and weights handed over by the gate/up
+//                             launch; one extra workgroup writes the routing
+//                             outputs (indices, weights, bucket layout)
 //
-// Every workgroup recomputing its token's top-k from the logits (a few
+// Every gate/up workgroup recomputing its token's top-k from the logits (a few
 // hundred 64-bit key compares per thread) is cheaper at decode than handing the
-// choice between workgroups, which costs several dependent memory round trips.
+// choice between workgroups of one launch, which costs several dependent memory
+// round trips; across the launch boundary to down/combine the hand-off is free
+// (its loads ride with the h loads), so that launch ranks nothing.
 //
 // Same arithmetic as the general path (router.hpp, stage.hpp, expert.hpp); the
 // layer's definition and the readings are cited there. Only the work split
@@ -298,14 +300,16 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
 // workgroup stages token t's A row in LDS and computes the 8 gate + 8 up rows
 // of row group rg of expert idx[p] for that single row (MFMA row 0), the waves
 // splitting the super-blocks (one each at H = 2048, so that each wave's chain
-// of dependent MFMAs is one super-block long). Output h[p][I] = SiLU(gate) * up.
+// of dependent MFMAs is one super-block long). Output h[p][I] = SiLU(gate) * up;
+// the first row group's workgroup also writes dsel[p] (the pair's expert) and
+// dw[p] (its renormalised router weight) for down_combine_small_kernel.
 constexpr int kGpWaves = 8;
 
 __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_t *__restrict__ GU, int ngroups, int nsb,
                                                           const double *__restrict__ logits, int E, int k,
                                                           const f16 *__restrict__ x_hilo, const f16 *__restrict__ x_xs,
                                                           const float *__restrict__ x_sinv, float *__restrict__ h,
-                                                          int I) {
+                                                          int I, int32_t *__restrict__ dsel, float *__restrict__ dw) {
     __shared__ __attribute__((aligned(16))) f16 arow[2 * kSmallMaxH];
     __shared__ __attribute__((aligned(16))) f16 axs[kSmallMaxH / kQ4Weights * 16];
     __shared__ float asv[kSmallMaxH / kQ4Weights];
@@ -331,12 +335,6 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
     // expert of pair p = t*k + j: slot j of token t's top-k
     topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
     const int e = sel_e[p - t * k];
-#pragma unroll
-    for (int i = 0; i < kRowLoads; ++i)
-        if (tid + NT * i < H / 4) ((u32x4 *)arow)[tid + NT * i] = xr[i];
-    if (tid < nsb * 4) ((u32x2 *)axs)[tid] = xsr;
-    if (tid < nsb) asv[tid] = svr;
-    __syncthreads();
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
 
     // wave w takes super-blocks w, w + kGpWaves, ...; two per pass
@@ -349,8 +347,27 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
             hd[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
         }
     };
+    // the weight loads go out as soon as the expert is known, ahead of the
+    // row's LDS stores and the barrier
     u32x4 q0[2], q1[2], hd[2];
     load_pass(wave, q0, q1, hd);
+#pragma unroll
+    for (int i = 0; i < kRowLoads; ++i)
+        if (tid + NT * i < H / 4) ((u32x4 *)arow)[tid + NT * i] = xr[i];
+    if (tid < nsb * 4) ((u32x2 *)axs)[tid] = xsr;
+    if (tid < nsb) asv[tid] = svr;
+    __syncthreads();
+    // hand the pair's expert and renormalised weight to the down/combine
+    // launch (one workgroup per pair), so that it need not rank the logits
+    // again before its weight loads
+    if (rg == 0 && wave == 0) {
+        const double ex = (lane < k) ? exp(sel_v[lane] - sel_v[0]) : 0.0;
+        const double z = wave_sum(ex);
+        if (lane == p - t * k) {
+            dsel[p] = e;
+            dw[p] = (float)(ex / z);
+        }
+    }
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const bool a_ok = (n == 0);  // the tile's only row
@@ -386,7 +403,8 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
 constexpr int kDcWaves = 12;       // waves per down/combine workgroup
 constexpr int kDcMaxUnits = 2;     // (slot, super-block) units a wave holds in flight
 
-// Grid (H/16 row groups + 1, T tokens), 512 threads. The k*nsb (slot j,
+// Grid (H/16 row groups + 1, T tokens), kDcWaves waves. The token's experts and
+// router weights come from gateup_pair_kernel (dsel, dw). The k*nsb (slot j,
 // super-block b) units of one token are spread over the waves; each unit
 // stages its 256 h values (row t*k + j of gateup_pair_kernel's output) in LDS (power-of-two scale, fp16 hi/lo, sub-block
 // sums), runs the row-0 MFMA tile against the down weights of expert idx[t][j]
@@ -394,7 +412,8 @@ constexpr int kDcMaxUnits = 2;     // (slot, super-block) units a wave holds in 
 // sum_j w[t][j] * sum_b partial[j][b] in slot order.
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     const uint8_t *__restrict__ Wd, int ngroups, int nsb, const double *__restrict__ logits, int E, int T, int k,
-    const float *__restrict__ h, int I, float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
+    const float *__restrict__ h, int I, const int32_t *__restrict__ dsel, const float *__restrict__ dw,
+    float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ entries, int32_t *__restrict__ pos) {
     const int rg = blockIdx.x, t = blockIdx.y;
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
         return;
     }
     // h rows are pair-indexed (t*k + j), so the first pass's h loads do not
-    // wait for the top-k: issued here, they are in flight with its logit loads
+    // wait for the routing: issued here, they are in flight with its loads
     float4 hv0[kDcMaxUnits];
 #pragma unroll
     for (int i = 0; i < kDcMaxUnits; ++i) {
@@ -425,15 +444,10 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
         const int j = u / nsb, b = u % nsb;
         hv0[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
     }
-    // the token's k experts and renormalised weights, lane j holding slot j
-    topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
-    const int my_e = sel_e[min(lane, k - 1)];
-    float my_w = 0.f;
-    if (wave == 0) {
-        const double ex = (lane < k) ? exp(sel_v[lane] - sel_v[0]) : 0.0;
-        const double z = wave_sum(ex);
-        my_w = (float)(ex / z);
-    }
+    // the token's k experts and renormalised weights, lane j holding slot j,
+    // as gateup_pair_kernel ranked them (loaded together with the h rows)
+    const int my_e = dsel[(size_t)t * k + min(lane, k - 1)];
+    const float my_w = lane < k ? dw[(size_t)t * k + lane] : 0.f;
     for (int base = 0; base < units; base += kDcWaves * kDcMaxUnits) {
         u32x4 q0[kDcMaxUnits], q1[kDcMaxUnits], hdr[kDcMaxUnits];
         float4 hv[kDcMaxUnits];

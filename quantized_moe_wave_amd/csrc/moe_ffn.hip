@@ -79,6 +79,8 @@ struct Workspace {
     f16 *h_xs = nullptr;          // [S][I/256][16]
     float *h_sinv = nullptr;      // [S][I/256]
     float *Y = nullptr;           // [S][H]
+    int32_t *dsel = nullptr;      // [S] decode path: expert of each (token, slot) pair
+    float *dw = nullptr;          // [S] decode path: its renormalised router weight
 };
 
 // 16-row tiles: only buckets of fewer than kGemmMinRows (<= 16) entries take
@@ -238,6 +240,8 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
     w->h_xs = (f16 *)take(S * ni * 16 * 2);
     w->h_sinv = (float *)take(S * ni * 4);
     w->Y = (float *)take(S * H * 4);
+    w->dsel = (int32_t *)take(S * 4);
+    w->dw = (float *)take(S * 4);
     return off;
 }
 
@@ -398,9 +402,10 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
                w.logits, w.x_hilo, w.x_xs, w.x_sinv);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
-               w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
+               w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
         launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
-               H / kRowGroup, ni, w.logits, E, T, k, w.h, I, out, H, idx, wt, w.counts, w.offsets, w.entries, w.pos);
+               H / kRowGroup, ni, w.logits, E, T, k, w.h, I, w.dsel, w.dw, out, H, idx, wt, w.counts, w.offsets,
+               w.entries, w.pos);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
         h->last_T = T;
