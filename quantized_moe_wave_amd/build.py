@@ -19,6 +19,10 @@ HIPCC_FLAGS = [
     "-fPIC",
     # keep the compiler from emitting packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the kernels rescale and update them
+    # with VALU instructions, which cannot read accumulator registers directly
+    # (otherwise every update moves them out and back)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall",
 ]
 

@@ -90,33 +90,12 @@ __device__ __forceinline__ void q_times_scale_pair(uint32_t dA, uint32_t dB, f16
     bhi[4] = h2[0]; bhi[5] = h2[1]; bhi[6] = h3[0]; bhi[7] = h3[1];
 }
 
-// As q_times_scale_pair, with the two scales as one packed pair sp =
-// {sc_lo, sc_hi} and their offsets np = {-1024 sc_lo, -64 sc_hi} (packed
-// forms cost one instruction per pair of sub-blocks instead of several per
-// scale).
-__device__ __forceinline__ void q_times_scale_pair_packed(uint32_t dA, uint32_t dB, f16x2 sp, f16x2 np, f16x8 &blo,
-                                                          f16x8 &bhi, const NibbleConsts &k) {
-    const uint32_t a8 = dA >> 8, b8 = dB >> 8;
-    const f16x2 s0 = {sp.x, sp.x}, n0 = {np.x, np.x};
-    const f16x2 s1 = {sp.y, sp.y}, n1 = {np.y, np.y};
-    const f16x2 l0 = __builtin_elementwise_fma(u32_as_f16x2((dA & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 0, 2
-    const f16x2 l1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 1, 3
-    const f16x2 l2 = __builtin_elementwise_fma(u32_as_f16x2((dB & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 4, 6
-    const f16x2 l3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & k.lo_mask) | k.lo_magic), s0, n0);  // bytes 5, 7
-    const f16x2 h0 = __builtin_elementwise_fma(u32_as_f16x2((dA & k.hi_mask) | k.hi_magic), s1, n1);
-    const f16x2 h1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & k.hi_mask) | k.hi_magic), s1, n1);
-    const f16x2 h2 = __builtin_elementwise_fma(u32_as_f16x2((dB & k.hi_mask) | k.hi_magic), s1, n1);
-    const f16x2 h3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & k.hi_mask) | k.hi_magic), s1, n1);
-    blo[0] = l0[0]; blo[1] = l0[1]; blo[2] = l1[0]; blo[3] = l1[1];
-    blo[4] = l2[0]; blo[5] = l2[1]; blo[6] = l3[0]; blo[7] = l3[1];
-    bhi[0] = h0[0]; bhi[1] = h0[1]; bhi[2] = h1[0]; bhi[3] = h1[1];
-    bhi[4] = h2[0]; bhi[5] = h2[1]; bhi[6] = h3[0]; bhi[7] = h3[1];
-}
-
 // Scales of sub-blocks 2i and 2i + 1 (bytes 2(i%2), 2(i%2) + 1 of the word w
-// holding four 6-bit scales) as the packed pair sp, and their offsets np as
-// in q_times_scale_pair_packed: a byte under exponent byte 0x64 is the half
-// 1024 + byte, so one permute and one packed subtract give both scales.
+// holding four 6-bit scales) as the packed pair sp, and the offsets the two
+// nibble halves remove, np = {-1024 sc_2i, -64 sc_2i+1} (see
+// q_times_scale_pair): a byte under exponent byte 0x64 is the half
+// 1024 + byte, so one permute, one packed subtract and one packed multiply
+// give both, instead of two conversions and a multiply per scale.
 __device__ __forceinline__ void scale_pair(uint32_t w, int i, f16x2 &sp, f16x2 &np) {
     const uint32_t raw = __builtin_amdgcn_perm(0x64646464u, w, (i & 1) ? 0x04030402u : 0x04010400u);
     const f16x2 k1024 = {(f16)1024.f, (f16)1024.f};
@@ -138,6 +117,22 @@ __device__ __forceinline__ f16x8 q_times_scale_nib(uint32_t dA, uint32_t dB, uin
     const f16x2 r1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & mask) | magic), s2, n2);  // bytes 1, 3
     const f16x2 r2 = __builtin_elementwise_fma(u32_as_f16x2((dB & mask) | magic), s2, n2);  // bytes 4, 6
     const f16x2 r3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & mask) | magic), s2, n2);  // bytes 5, 7
+    f16x8 out;
+    out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
+    out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];
+    return out;
+}
+
+// q_times_scale_nib with the scale and offset already in fp16 (sc2 = {sc, sc},
+// n2 = {-1024 sc, -1024 sc} for NIB 0, {-64 sc, -64 sc} for NIB 1).
+template <int NIB>
+__device__ __forceinline__ f16x8 q_times_scale_nib_sn(uint32_t dA, uint32_t dB, uint32_t a8, uint32_t b8, f16x2 sc2,
+                                                      f16x2 n2, const NibbleConsts &k) {
+    const uint32_t mask = NIB ? k.hi_mask : k.lo_mask, magic = NIB ? k.hi_magic : k.lo_magic;
+    const f16x2 r0 = __builtin_elementwise_fma(u32_as_f16x2((dA & mask) | magic), sc2, n2);  // bytes 0, 2
+    const f16x2 r1 = __builtin_elementwise_fma(u32_as_f16x2((a8 & mask) | magic), sc2, n2);  // bytes 1, 3
+    const f16x2 r2 = __builtin_elementwise_fma(u32_as_f16x2((dB & mask) | magic), sc2, n2);  // bytes 4, 6
+    const f16x2 r3 = __builtin_elementwise_fma(u32_as_f16x2((b8 & mask) | magic), sc2, n2);  // bytes 5, 7
     f16x8 out;
     out[0] = r0[0]; out[1] = r0[1]; out[2] = r1[0]; out[3] = r1[1];
     out[4] = r2[0]; out[5] = r2[1]; out[6] = r3[0]; out[7] = r3[1];

@@ -267,15 +267,24 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             o[cb] = u32x4{a, b, a >> 8, b >> 8};
         }
     };
+    // fp16 scales and offsets of chunk q's two sub-blocks (2q, 2q + 1) in each
+    // group: computed once per chunk, used by its two k-steps
+    struct ScalePairs {
+        f16x2 sp[CW], np[CW];
+    };
+    auto scale_pairs = [&](int q, const Scales &kk, ScalePairs &pp) {
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) scale_pair(q < 2 ? kk.lo[cb] : kk.hi[cb], q, pp.sp[cb], pp.np[cb]);
+    };
     // B fragments of k-step 2q + s2: sub-block scale x quant (low nibbles for
     // s2 = 0, high for s2 = 1)
-    auto build_b_half = [&](int q, int s2, const Scales &kk, const u32x4 (&w)[CW], f16x8 (&Bf)[CW]) {
+    auto build_b_half = [&](int s2, const ScalePairs &pp, const u32x4 (&w)[CW], f16x8 (&Bf)[CW]) {
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
-            const uint32_t scw = q < 2 ? kk.lo[cb] : kk.hi[cb];
-            const f16 sc = (f16)(float)((scw >> (16 * (q & 1) + 8 * s2)) & 0xFFu);
-            Bf[cb] = s2 ? q_times_scale_nib<1>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc, nk)
-                        : q_times_scale_nib<0>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc, nk);
+            const f16 sc = s2 ? pp.sp[cb].y : pp.sp[cb].x, nc = s2 ? pp.np[cb].y : pp.np[cb].x;
+            const f16x2 sc2 = {sc, sc}, n2 = {nc, nc};
+            Bf[cb] = s2 ? q_times_scale_nib_sn<1>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc2, n2, nk)
+                        : q_times_scale_nib_sn<0>(w[cb].x, w[cb].y, w[cb].z, w[cb].w, sc2, n2, nk);
         }
     };
 
@@ -347,6 +356,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     __builtin_amdgcn_sched_barrier(0);
 
     Scales kc;
+    ScalePairs kp;  // of the chunk whose k-steps are being built
     f16x8 Ah0[RB], Al0[RB], B0[CW], Ah1[RB], Al1[RB], B1[CW];
     u32x4 wq[CW];
     u32x4 wfull[CW];  // quants of the current half super-block
@@ -354,7 +364,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     read_quants(0, wfull);
     quants_of(wfull, false, wq);
     read_a_half(0, 0, Ah0, Al0);
-    build_b_half(0, 0, kc, wq, B0);
+    scale_pairs(0, kc, kp);
+    build_b_half(0, kp, wq, B0);
     __builtin_amdgcn_sched_barrier(0);
 
     // Super-block b's min term and its rescale are spread over its
@@ -434,7 +445,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             }
             if (q == 1) min_term(b);
             read_a_half(c, 1, Ah1, Al1);
-            build_b_half(q, 1, kc, wq, B1);
+            build_b_half(1, kp, wq, B1);
             mfma_half(Ah0, Al0, B0);
             interleave(0);
             pin(B1);
@@ -474,7 +485,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                 if ((q & 1) != 0) read_quants((c + 1) >> 1, wfull);  // chunk c+1 starts a half super-block
                 quants_of(wfull, ((q + 1) & 1) != 0, wn);
                 read_a_half(c + 1, 0, Ah0, Al0);
-                build_b_half((q + 1) & 3, 0, kc, wn, B0);
+                scale_pairs((q + 1) & 3, kc, kp);
+                build_b_half(0, kp, wn, B0);
 #pragma unroll
                 for (int cb = 0; cb < CW; ++cb) wq[cb] = wn[cb];
             }
@@ -494,8 +506,16 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
 }
 
+// Waves per SIMD the register budget is sized for: big tiles run one
+// workgroup per CU (NW / 4 waves per SIMD); 16-row tiles two (their LDS allows
+// two workgroups), so they must fit 256 registers (with a budget of 512 the
+// compiler parks values in accumulator registers and moves them back and forth).
+template <int RB, int NW>
+constexpr int gemm_waves_per_simd() { return RB == 1 ? 2 : NW / 4; }
+
 template <bool GATEUP, int RB, int CW, int NW>
-__global__ __launch_bounds__(64 * NW, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4))) void expert_gemm_kernel(
+__global__ __launch_bounds__(64 * NW, 1) __attribute__((
+    amdgpu_waves_per_eu(gemm_waves_per_simd<RB, NW>(), gemm_waves_per_simd<RB, NW>()))) void expert_gemm_kernel(
     const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
     const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
