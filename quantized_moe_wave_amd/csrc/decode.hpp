@@ -52,10 +52,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
 
 // One wave per expert (waves 0 .. E-1 of the grid) and one per (token,
 // super-block) staging unit of x (the T*nsb waves after them), so that no
-// wave does both one after the other. COHERENT: logits are stored with
-// agent-scope atomic stores (read back by another workgroup of the same
-// launch).
-template <bool COHERENT>
+// wave does both one after the other.
 __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, const float *__restrict__ wr,
                                                   const float *__restrict__ bias, int T, int H, int E,
                                                   double *__restrict__ logits, f16 *__restrict__ x_hilo,
@@ -110,11 +107,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                 double s = wave_sum(acc[t]);
                 if (lane == 0) {
                     if (bias) s += (double)bias[e];
-                    if (COHERENT)
-                        __hip_atomic_store(&logits[(size_t)t * E + e], s, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    else
-                        logits[(size_t)t * E + e] = s;
+                    logits[(size_t)t * E + e] = s;
                 }
             }
         }
@@ -132,7 +125,6 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
 // waves 2-3 j >= 64; for larger E candidate c = tid counts all 256. The
 // thread that writes a winner is the one that loaded it (tid == c). lg: 256
 // LDS words of 8 bytes, which hold the keys.
-template <bool COHERENT>
 __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, double *lg, int *sel_e,
                                            double *sel_v) {
     __shared__ int rk_hi[128];
@@ -141,9 +133,8 @@ __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, dou
     const bool act = tid < 256;  // threads past 256 (larger workgroups) only join the barriers
     double v = -INFINITY;
     if (act) {
-        // COHERENT: written by other workgroups of this launch (agent-scope load)
         const int c = min(tid, E - 1);
-        const double x = COHERENT ? __hip_atomic_load(&lrow[c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : lrow[c];
+        const double x = lrow[c];
         v = (tid < E && x == x) ? x : -INFINITY;
         keys[tid] = rank_key(v, tid);
     }
@@ -180,7 +171,6 @@ __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, dou
 // Routing outputs of all T tokens: idx/w per token, then the stable bucket
 // layout of the T*k <= 256 pairs, the latter by wave 0 alone (lane l owns
 // experts 4l .. 4l+3, E <= 256).
-template <bool COHERENT>
 __device__ __forceinline__ void routing_outputs_small(const double *logits, int T, int E, int k, double *lg, int *sel_e,
                                                    double *sel_v, int32_t *idx_out, float *w_out, int32_t *counts,
                                                    int32_t *offsets, int32_t *entries, int32_t *pos) {
@@ -188,7 +178,7 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
     __shared__ int off_l[kRankMaxExperts];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     for (int t = 0; t < T; ++t) {
-        topk_block<COHERENT>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
+        topk_block(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
         if (wave == 0) {
             const double ex = (lane < k) ? exp(sel_v[lane] - sel_v[0]) : 0.0;
             const double z = wave_sum(ex);
@@ -253,7 +243,7 @@ __global__ __launch_bounds__(64) void router_small_kernel(const float *__restric
                                                            const float *__restrict__ bias, int T, int H, int E,
                                                            double *__restrict__ logits, f16 *__restrict__ x_hilo,
                                                            f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
-    logits_small_body<false>(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv);
+    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv);
 }
 
 constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS
@@ -333,7 +323,7 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
     const u32x2 xsr = ((const u32x2 *)(x_xs + (size_t)t * nsb * 16))[min(tid, nsb * 4 - 1)];
     const float svr = x_sinv[(size_t)t * nsb + min(tid, nsb - 1)];
     // expert of pair p = t*k + j: slot j of token t's top-k
-    topk_block<false>(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
+    topk_block(logits + (size_t)t * E, E, k, lg, sel_e, sel_v);
     const int e = sel_e[p - t * k];
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
 
@@ -431,8 +421,8 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     // The extra column of workgroups (rg == H/16) has no down rows: the first
     // one writes the routing outputs of all T tokens, the others leave.
     if (rg == ngroups) {
-        if (t == 0) routing_outputs_small<false>(logits, T, E, k, lg, sel_e, sel_v, idx_out, w_out, counts, offsets,
-                                                 entries, pos);
+        if (t == 0)
+            routing_outputs_small(logits, T, E, k, lg, sel_e, sel_v, idx_out, w_out, counts, offsets, entries, pos);
         return;
     }
     // h rows are pair-indexed (t*k + j), so the first pass's h loads do not
