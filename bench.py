@@ -17,6 +17,8 @@ its roofline fraction uses algorithmic bytes (decode: routed gate+up Q4_K
 weight bytes) or flops (prefill: 2*T*k*2*H*I) per launch.
 
 The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
+For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
+(the decode kernels' weight bytes) the same way.
 
 The CPU baseline is the fp64 oracle as it stands, timed on this host on a
 bounded sample of the same workload.
@@ -328,6 +330,37 @@ def cpu_baseline(inp, seconds: float):
             "sample": f"{n} single-token forwards of the {wl.name} layer (replica 0 weights), {el:.1f} s"}
 
 
+def copy_probe(sizes_mb=(7, 14, 21), steps: int = 200) -> dict:
+    """Context for the decode roofline: a plain device copy (torch) of the decode kernels' byte counts, timed like a
+    step (one HIP graph of `steps` copies cycling over >= 1 GB of sources, so the caches are cold)."""
+    import torch
+
+    out = {}
+    for mb in sizes_mb:
+        n = mb * (1 << 20) // 4
+        R = max(4, REPLICA_BYTES // (n * 4))
+        src = [torch.randn(n, device="cuda") for _ in range(R)]
+        dst = [torch.empty(n, device="cuda") for _ in range(R)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                dst[i % R].copy_(src[i % R])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out[f"{mb}MiB"] = {"us": round(us, 2), "read_GBs": round(n * 4 / us / 1e3, 1)}
+        del src, dst, g
+        torch.cuda.empty_cache()
+    log(f"plain copy probe: {out}")
+    return out
+
+
 def copy_calibration(mb: int) -> None:
     import torch
 
@@ -406,6 +439,7 @@ def main() -> int:
             "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
             "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof,
         }
+    line["hbm_step"]["plain_copy_probe"] = copy_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]
     if extras:
         line["others"] = [measure_step(synth.WORKLOADS[w], args.extra_steps, args.eager, args.stages) for w in extras]
