@@ -243,9 +243,14 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
                     "kernel": f"{kname} ({stage})", "avg_us": round(total_ms / launches * 1e3, 3),
                     "algorithmic_bytes_per_launch": int(round(alg / launches))}
         else:
-            # prefill: the gate/up grouped GEMM; 2 * rows * 2I * H flops per launch
+            # prefill: the gate/up grouped GEMM (its 8-wave launch plus the 4-wave launch that runs the split
+            # last-round tiles, when there is one); 2 * rows * 2I * H flops per step
+            import quantized_moe_wave_amd as q
+
             stage = "gate_up_big"
-            prof = b.stage_times(steps, [stage])[stage]
+            tail = "gate_up_tail" if "gate_up_tail" in q.moe_ffn_stage_names() else None
+            both = b.stage_times(steps, [stage] + ([tail] if tail else []))
+            prof = [(r, ms + (both[tail][i][1] if tail else 0.0), nl) for i, (r, ms, nl) in enumerate(both[stage])]
             total_ms = sum(p[1] for p in prof)
             launches = sum(p[2] for p in prof)
             if launches == 0 or total_ms <= 0:
@@ -255,7 +260,7 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
             roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                     "traffic": measured_traffic("expert_gemm_kernel<gate_up, 64-row tiles>"),
-                    "kernel": "expert_gemm_kernel<gate_up, 64-row tiles> (gate_up_big)",
+                    "kernel": "expert_gemm_kernel<gate_up, 64-row tiles> (gate_up_big + gate_up_tail)",
                     "avg_us": round(total_ms / launches * 1e3, 3)}
         avg_us = total_ms / launches * 1e3
         log(f"{wl.name}: {stage} avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")

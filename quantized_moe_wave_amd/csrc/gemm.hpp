@@ -506,6 +506,28 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
 }
 
+// Last-round balance of a big-tile launch. Per XCD x the launch has n_x =
+// tiles_x * ncb units (tile, column block of 2*16 weight groups at 8 waves),
+// run one per CU, C CUs at a time; n_x % C units would make a last round that
+// leaves most of the XCD idle. When those r_x units fit C as halves (2 r_x <=
+// C), the launch skips them (mode 1) and a second launch of the 4-wave
+// instance runs each as two independent half-width units (mode 2), so the
+// last round is half as long; outputs do not overlap, nothing is summed.
+struct TailSplit {
+    int per_xcd;  // tiles per XCD (a contiguous range of the tile list)
+    int full_x;   // units the main launch runs
+    int r_x;      // units split into halves (0: none)
+};
+__device__ __forceinline__ TailSplit tail_split(int ntl, int ncb, int x, int C) {
+    TailSplit t;
+    t.per_xcd = (ntl + 7) >> 3;
+    const int n_x = max(0, min(t.per_xcd, ntl - x * t.per_xcd)) * ncb;
+    const int r = C > 0 ? n_x % C : 0;
+    t.r_x = (r > 0 && 2 * r <= C) ? r : 0;
+    t.full_x = n_x - t.r_x;
+    return t;
+}
+
 // Waves per SIMD the register budget is sized for: big tiles run one
 // workgroup per CU (NW / 4 waves per SIMD); 16-row tiles two (their LDS allows
 // two workgroups), so they must fit 256 registers (with a budget of 512 the
@@ -518,7 +540,8 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((
     amdgpu_waves_per_eu(gemm_waves_per_simd<RB, NW>(), gemm_waves_per_simd<RB, NW>()))) void expert_gemm_kernel(
     const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
-    const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld) {
+    const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld, int C,
+    int mode) {
     using Sh = GemmShape<RB, CW, NW>;
     constexpr int NT = 64 * NW;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -528,19 +551,31 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((
     uint8_t *xsbuf = hbuf + 2 * Sh::HdrBuf;
     float *svbuf = (float *)(smem + Sh::SvOff);
 
-    const int ncb = ngroups / Sh::Groups;
+    // unit of this workgroup (tail_split): mode 0 every unit of this launch,
+    // 1 all but the XCD's split tail units, 2 (the 4-wave instance) the
+    // halves of the 8-wave launch's split units
     const int ntl = *n_tiles;
-    const int per_xcd = (ntl + 7) >> 3;  // tiles per XCD (a contiguous range)
-    const int slot_id = blockIdx.x >> 3;
-    const int tile = (blockIdx.x & 7) * per_xcd + slot_id / ncb;
-    const int cblk = slot_id % ncb;
-    if (slot_id / ncb >= per_xcd || tile >= ntl) return;
+    const int x = blockIdx.x & 7, sid = blockIdx.x >> 3;
+    int tile, rg0;
+    if (mode == 2) {
+        const int ncb8 = ngroups / (2 * Sh::Groups);
+        const TailSplit ts = tail_split(ntl, ncb8, x, C);
+        if (sid >= 2 * ts.r_x) return;
+        const int u = ts.full_x + (sid >> 1);
+        tile = x * ts.per_xcd + u / ncb8;
+        rg0 = (u % ncb8) * 2 * Sh::Groups + (sid & 1) * Sh::Groups;
+    } else {
+        const int ncb = ngroups / Sh::Groups;
+        const TailSplit ts = tail_split(ntl, ncb, x, mode == 1 ? C : 0);
+        if (sid >= ts.full_x) return;
+        tile = x * ts.per_xcd + sid / ncb;
+        rg0 = (sid % ncb) * Sh::Groups;
+    }
     const u32x4 tr = *(const u32x4 *)&tiles[tile];
     const int e = (int)tr.x, r0 = (int)tr.y, rows = (int)tr.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: LDS addresses stay scalar
     const int n = lane & 15, g = lane >> 4;
-    const int rg0 = cblk * Sh::Groups;
 
     f32x4 X[RB][CW];
     float fcur[CW];

@@ -99,10 +99,13 @@ enum Stage {
     kStDown,
     kStDownBig,
     kStCombine,
+    kStGateUpTail,
+    kStDownTail,
     kStCount
 };
-const char *const kStageNames[kStCount] = {"router",      "topk",    "bucket", "stage_x",  "gate_up",
-                                           "gate_up_big", "stage_h", "down",   "down_big", "combine"};
+const char *const kStageNames[kStCount] = {"router",      "topk",    "bucket",   "stage_x",  "gate_up",
+                                           "gate_up_big", "stage_h", "down",     "down_big", "combine",
+                                           "gate_up_tail", "down_tail"};
 
 // Start/stop events of profiled stages. A profiled kernel is launched with
 // hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
@@ -161,6 +164,7 @@ void launch(Profiler &pf, int s, void (*kernel)(KArgs...), dim3 grid, dim3 block
 struct moe_ffn_s {
     moe_ffn_shape sh{};
     int device = -1;
+    int cus_per_xcd = 0;     // compute units per XCD (0: the big GEMMs' last round is not split)
     uint8_t *gu = nullptr;   // repacked gate/up
     uint8_t *dn = nullptr;   // repacked down
     float *rw = nullptr;     // [E][H]
@@ -312,12 +316,14 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
         return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
     hipStream_t hs = (hipStream_t)stream;
     {
-        const hipError_t a[5] = {
+        const hipError_t a[6] = {
             hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
             hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
             hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
             hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds),
@@ -335,6 +341,13 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
         return r;
     };
     if (hipGetDevice(&h->device) != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "hipGetDevice failed"));
+    {
+        // the big GEMMs' tail split assumes workgroups spread round-robin over 8 XCDs of equal size
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, h->device) != hipSuccess)
+            return cleanup(fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed"));
+        h->cus_per_xcd = prop.multiProcessorCount % 8 == 0 ? prop.multiProcessorCount / 8 : 0;
+    }
     const int E = s.num_experts, H = s.hidden_dim, I = s.moe_intermediate;
     if (hipMalloc(&h->gu, 2 * gb) != hipSuccess || hipMalloc(&h->dn, db) != hipSuccess ||
         hipMalloc(&h->rw, (size_t)E * H * 4) != hipSuccess ||
@@ -461,29 +474,44 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     using Small = GemmShape<1, 4, 4>;
     using Big = GemmShape<4, 4, 8>;
     using BigN = GemmShape<4, 4, 4>;
+    // big tiles: the 8-wave launch leaves each XCD's split tail units (see
+    // tail_split in gemm.hpp) to a 4-wave launch that runs them as halves;
+    // only where there are enough pairs for several big tiles per XCD (with
+    // few or none the extra launch costs more than it saves)
+    const int C = S >= (size_t)E * kGemmMinRows ? h->cus_per_xcd : 0;
     launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4, 4>, dim3(8 * (gu_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
-               w.x_xs, w.x_sinv, w.h, I);
-    if (S >= kGemmMinRows)
+               w.x_xs, w.x_sinv, w.h, I, 0, 0);
+    if (S >= kGemmMinRows) {
         launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 4, 8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
                    dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
-                   w.x_hilo, w.x_xs, w.x_sinv, w.h, I);
+                   w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
+        if (C > 0)
+            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 4, 4>, dim3(8 * C), dim3(256), BigN::Lds, st,
+                       h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
+                       w.h, I, C, 2);
+    }
 
     launch(pf, kStStageH, stage_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo, w.h_xs,
            w.h_sinv);
 
     launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4, 4>, dim3(8 * (dn_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
-               w.h_xs, w.h_sinv, w.Y, H);
+               w.h_xs, w.h_sinv, w.Y, H, 0, 0);
     if (S >= kGemmMinRows) {
-        if (gemm_big_waves(dn_groups) == 8)
+        if (gemm_big_waves(dn_groups) == 8) {
             launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8>,
                        dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
-                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
-        else
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, C, 1);
+            if (C > 0)
+                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 4, 4>, dim3(8 * C), dim3(256), BigN::Lds,
+                           st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs,
+                           w.h_sinv, w.Y, H, C, 2);
+        } else {
             launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 4>,
                        dim3(8 * (dn_groups / BigN::Groups) * mg8), dim3(256), BigN::Lds, st, h->dn, dn_groups, ni,
-                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H);
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, 0, 0);
+        }
     }
 
     launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
