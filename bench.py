@@ -16,6 +16,10 @@ steps with events stamped at its own start and end (hipExtLaunchKernelGGL);
 its roofline fraction uses algorithmic bytes (decode: routed gate+up Q4_K
 weight bytes) or flops (prefill: 2*T*k*2*H*I) per launch.
 
+Single eager steps (median, 10th / 90th percentile) go under "step_us": "warm" with
+only a GPU sleep between steps, "cold" with a 512 MB write between steps (outside
+the timed events) that leaves no weight or input in any cache.
+
 The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
 For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
 (the decode kernels' weight bytes) the same way.
@@ -158,6 +162,37 @@ class Bench:
         del gw, gt
         return ms
 
+    def per_step(self, n: int, flush_mb: int = 512) -> dict:
+        """Median and 10th / 90th percentile of single-step times (us): n eager steps, cycling over the replicas,
+        each between two events. "warm": a GPU sleep (no memory traffic) before each step, long enough for the host
+        to have queued the step before it starts; "cold": a write of flush_mb MB before each step (outside the
+        events), so no weight or input is left in L2 or the Infinity Cache."""
+        import numpy as np
+        import torch
+
+        flush = torch.empty(flush_mb * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+        res = {}
+        for mode in ("warm", "cold"):
+            for r in range(self.R):
+                self.step(r)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+            for i in range(n):
+                if mode == "cold":
+                    flush.fill_(float(i))
+                else:
+                    torch.cuda._sleep(200_000)
+                ev[i][0].record()
+                self.step(i)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            us = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+            res[mode] = {"median": round(float(np.median(us)), 2), "p10": round(float(np.percentile(us, 10)), 2),
+                         "p90": round(float(np.percentile(us, 90)), 2), "steps": n}
+        del flush
+        res["flush_mb"] = flush_mb
+        log(f"{self.wl.name}: single-step us {res}")
+        return res
+
     def stage_times(self, steps: int, stages) -> dict:
         """{stage: [(replica, total ms, launches)]} from kernel-stamped events over `steps` eager steps."""
         import torch
@@ -273,7 +308,8 @@ def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: b
                 n = sum(p[2] for p in lst)
                 log(f"{wl.name}: stage {s:8s} {tm / max(n, 1) * 1e3:9.2f} us avg over {n} launches")
         U = sum(st[0] for st in stats) / len(stats)
-        return b, ms, stats, roof, U
+        roof_steps = b.per_step(max(20, min(steps, 200)))
+        return b, ms, stats, roof, U, roof_steps
     except Exception:
         b.close()
         raise
@@ -400,7 +436,7 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     wl = synth.WORKLOADS[args.workload]
-    b, ms, stats, roof, U = measure(wl, args.steps, args.warmup, args.eager, "hbm", args.stages)
+    b, ms, stats, roof, U, dist = measure(wl, args.steps, args.warmup, args.eager, "hbm", args.stages)
     host0 = b.host0
     b.close()
     del b
@@ -427,10 +463,11 @@ def main() -> int:
                      "unit": "GB/s", "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "distinct_experts": U},
         "roofline": roof,
+        "step_us": dist,
     }
     if not args.no_prefill:
         pw = synth.WORKLOADS[args.prefill_workload]
-        pb, pms, pstats, proof, pU = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager,
+        pb, pms, pstats, proof, pU, pdist = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager,
                                              "mfma", args.stages)
         pb.close()
         del pb
@@ -442,7 +479,7 @@ def main() -> int:
             "tflops": round(flops / (pms * 1e-3) / 1e12, 2),
             "frac_mfma_peak": round(flops / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
             "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
-            "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof,
+            "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof, "step_us": pdist,
         }
     line["hbm_step"]["plain_copy_probe"] = copy_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]
