@@ -61,6 +61,8 @@ def load():
     lib.mo_expert_q4k.restype = ctypes.c_int
     lib.mo_forward.argtypes = [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
     lib.mo_forward.restype = ctypes.c_int
+    lib.mo_rms_norm.argtypes = [i32, i32, vp, vp, f64, vp]
+    lib.mo_add_residual.argtypes = [i64, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -197,3 +199,36 @@ def forward(x, router_w, bias, gate, up, down, k: int, sel=None, idx_in=None):
     if rc != 0:
         raise ValueError("oracle forward rejected its arguments or ran out of memory")
     return {"out": out, "idx": idx, "w": wts, "logits": logits}
+
+
+def rms_norm(x, g, eps: float) -> np.ndarray:
+    """Pre-FFN RMSNorm of fp32 rows x [T][H] with weight g [H]: float64 [T][H]."""
+    x = np.ascontiguousarray(x, np.float32)
+    g = np.ascontiguousarray(g, np.float32)
+    T, H = x.shape
+    y = np.empty((T, H), np.float64)
+    load().mo_rms_norm(T, H, _ptr(x), _ptr(g), float(eps), _ptr(y))
+    return y
+
+
+def add_residual(hidden, ffn) -> np.ndarray:
+    """hidden (fp32) + ffn (float64), in float64."""
+    hidden = np.ascontiguousarray(hidden, np.float32)
+    ffn = np.ascontiguousarray(ffn, np.float64)
+    assert hidden.shape == ffn.shape
+    out = np.empty(hidden.shape, np.float64)
+    load().mo_add_residual(hidden.size, _ptr(hidden), _ptr(ffn), _ptr(out))
+    return out
+
+
+def block(hidden, norm_w, eps: float, router_w, bias, gate, up, down, k: int, sel=None):
+    """The layer inside its block: out = hidden + layer(rms_norm(hidden)). The normalised rows enter the layer as
+    fp32 (rounded to nearest), the type of the activation vectors the block passes between its steps.
+    Returns forward()'s dict with out replaced by the block output (rows `sel` if given) and "xn" added."""
+    hidden = np.ascontiguousarray(hidden, np.float32)
+    xn = rms_norm(hidden, norm_w, eps).astype(np.float32)
+    r = forward(xn, router_w, bias, gate, up, down, k, sel=sel)
+    rows = hidden if sel is None else hidden[np.asarray(sel)]
+    r["out"] = add_residual(rows, r["out"])
+    r["xn"] = xn
+    return r

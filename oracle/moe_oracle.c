@@ -350,3 +350,27 @@ done:
     free(logits); free(idx); free(w); free(Y); free(Wg); free(Wu); free(Wd);
     return rc;
 }
+
+/* ------------------------------------------------- the block around the layer */
+
+/* Pre-FFN norm (forward_qwen3_moe.rs: prefill step 2f and decode step 2g,
+ * "Pre-FFN norm"): the block normalises the residual stream with the layer's
+ * ffn norm weight and the model's eps before the MoE layer. The pages call the
+ * op (rms_norm) without writing out its formula; the standard RMSNorm is taken:
+ *   y[t][i] = x[t][i] * g[i] / sqrt((1/H) * sum_c x[t][c]^2 + eps). */
+void mo_rms_norm(int32_t T, int32_t H, const float *x, const float *g, double eps, double *y) {
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = x + t * H;
+        double ss = 0.0;
+        for (int32_t c = 0; c < H; ++c) ss += (double)row[c] * (double)row[c];
+        const double rms = sqrt(ss / (double)H + eps);
+        for (int32_t c = 0; c < H; ++c) y[t * H + c] = (double)row[c] * (double)g[c] / rms;
+    }
+}
+
+/* Residual after the layer (forward_qwen3_moe.rs: the "Residual" step after
+ * prefill step 2g, decode step 2i): the layer's output is added to the
+ * residual stream it was computed from, out = hidden + ffn. */
+void mo_add_residual(int64_t n, const float *hidden, const double *ffn, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = (double)hidden[i] + ffn[i];
+}

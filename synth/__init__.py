@@ -46,6 +46,8 @@ Q4K_BLOCK_WEIGHTS = 256
 TENSOR_X = 0
 TENSOR_ROUTER = 1
 TENSOR_EXPERTS = 2
+TENSOR_NORM = 3
+NORM_EPS = 1e-6  # the RMSNorm eps of the Qwen3-MoE models
 
 
 @dataclasses.dataclass(frozen=True)
@@ -104,6 +106,12 @@ def gen_bias(experts: int, zipf: float) -> np.ndarray | None:
         return None
     e = np.arange(experts, dtype=np.float64)
     return (-zipf * np.log(e + 1.0)).astype(np.float32)
+
+
+def gen_norm(seed: int, replica: int, hidden: int) -> np.ndarray:
+    """Pre-FFN norm weight [H] fp32, uniform in [0.5, 1.5)."""
+    g = rng(seed, replica, TENSOR_NORM)
+    return (0.5 + g.random(hidden, dtype=np.float64)).astype(np.float32)
 
 
 def _random_bytes(g: np.random.Generator, n: int) -> np.ndarray:
