@@ -116,6 +116,34 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
 moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                            int32_t *router_idx, void *stream);
 
+/* Set the pre-FFN norm of the block around the layer: the RMSNorm weight and
+ * eps that moe_ffn_forward_block applies (forward_qwen3_moe.rs, prefill step
+ * 2f and decode step 2g, "Pre-FFN norm": the residual stream is normalised
+ * with the layer's ffn norm weight and the model's eps before the MoE layer).
+ *   norm_w  [H] fp32, host or device pointer; copied (the caller keeps it).
+ *   eps     finite, >= 0 (Qwen3-MoE models use 1e-6).
+ * Synchronises stream. May be called again to replace the weight.
+ * Errors: INVALID_ARG (bad handle, NULL norm_w, eps negative or not finite),
+ * OOM, DEVICE. */
+moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *stream);
+
+/* The layer inside its block on T tokens of the residual stream:
+ *   out[t] = hidden[t] + layer(rms_norm(hidden[t]))
+ * with rms_norm(x)[i] = x[i] * norm_w[i] / sqrt(mean_c x[c]^2 + eps) (the
+ * standard RMSNorm; the pages name the op without its formula), rounded to
+ * fp32 as the layer's input, and the residual add of the block after the MoE
+ * FFN (forward_qwen3_moe.rs: the "Residual" step after prefill step 2g,
+ * decode step 2i). The norm is a launch of its own; the residual add happens
+ * in the kernel that writes out.
+ *   hidden      [T][H] fp32 residual stream.
+ *   out         [T][H] fp32 block output. Must not overlap hidden.
+ *   router_out, router_idx, stream: as for moe_ffn_forward (routing of the
+ *               normalised rows).
+ * Errors: as moe_ffn_forward, and INVALID_ARG if moe_ffn_set_norm has not been
+ * called on this handle. */
+moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, float *out, float *router_out,
+                                 int32_t *router_idx, void *stream);
+
 /* Copy the routing state of the most recent forward on this handle (for tests):
  *   logits  [T][E] fp64 router logits (bias included), or NULL;
  *   counts  [E] int32 tokens per expert, or NULL;
@@ -133,7 +161,9 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
  * launch does not stage x), 4 gate_up (16-row tiles of buckets of at most 16 entries, or the
  * per-pair decode kernel), 5 gate_up_big (tiles of up to 64 rows for larger
  * buckets), 6 stage_h, 7 down (16-row tiles, or the fused decode down +
- * combine), 8 down_big, 9 combine; a stage a forward does not run has no
+ * combine), 8 down_big, 9 combine, 10 gate_up_tail and 11 down_tail (the
+ * 64-row GEMMs' last-round tiles as half-width units), 12 norm (the RMSNorm of
+ * moe_ffn_forward_block); a stage a forward does not run has no
  * launches (moe_ffn_stage_name gives the name, moe_ffn_stage_count the number).
  * moe_ffn_profile sets a bit mask of stages; while it is non-zero, each forward
  * records a HIP event on its stream right before and right after every

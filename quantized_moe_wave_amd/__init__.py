@@ -11,8 +11,10 @@ from .binding import (  # noqa: F401
     moe_ffn_debug_routing,
     moe_ffn_destroy,
     moe_ffn_forward,
+    moe_ffn_forward_block,
     moe_ffn_profile,
     moe_ffn_profile_read,
     moe_ffn_stage_names,
     moe_ffn_reserve,
+    moe_ffn_set_norm,
 )

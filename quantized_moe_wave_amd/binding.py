@@ -38,6 +38,10 @@ _lib.moe_ffn_reserve.argtypes = [_vp, ctypes.c_int32, _vp]
 _lib.moe_ffn_reserve.restype = ctypes.c_int
 _lib.moe_ffn_forward.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_forward.restype = ctypes.c_int
+_lib.moe_ffn_set_norm.argtypes = [_vp, _vp, ctypes.c_float, _vp]
+_lib.moe_ffn_set_norm.restype = ctypes.c_int
+_lib.moe_ffn_forward_block.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_forward_block.restype = ctypes.c_int
 _lib.moe_ffn_debug_routing.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_debug_routing.restype = ctypes.c_int
 _lib.moe_ffn_destroy.argtypes = [_vp]
@@ -134,6 +138,31 @@ def moe_ffn_forward(handle: int, x: torch.Tensor, out: torch.Tensor, router_out:
     _check(st, "moe_ffn_forward")
 
 
+def moe_ffn_set_norm(handle: int, norm_w: torch.Tensor, eps: float, stream=None) -> None:
+    """Pre-FFN RMSNorm weight [hidden_dim] fp32 (CPU or GPU tensor; copied) and eps of moe_ffn_forward_block."""
+    if norm_w.dtype != torch.float32 or not norm_w.is_contiguous() or norm_w.dim() != 1:
+        raise TypeError("norm_w must be a contiguous 1-D float32 tensor")
+    st = _lib.moe_ffn_set_norm(_vp(handle), _vp(norm_w.data_ptr()), float(eps), _stream(stream))
+    _check(st, "moe_ffn_set_norm")
+
+
+def moe_ffn_forward_block(handle: int, hidden: torch.Tensor, out: torch.Tensor,
+                          router_out: torch.Tensor | None = None, router_idx: torch.Tensor | None = None,
+                          stream=None) -> None:
+    """out[T][H] <- hidden + MoE FFN of rms_norm(hidden); router_out/router_idx [T][k] optional."""
+    _dev(hidden, "hidden", torch.float32)
+    _dev(out, "out", torch.float32)
+    if hidden.dim() != 2 or out.shape != hidden.shape:
+        raise ValueError("hidden and out must both be [T, hidden_dim]")
+    if router_out is not None:
+        _dev(router_out, "router_out", torch.float32)
+    if router_idx is not None:
+        _dev(router_idx, "router_idx", torch.int32)
+    st = _lib.moe_ffn_forward_block(_vp(handle), int(hidden.shape[0]), _ptr(hidden), _ptr(out), _ptr(router_out),
+                                    _ptr(router_idx), _stream(stream))
+    _check(st, "moe_ffn_forward_block")
+
+
 def moe_ffn_debug_routing(handle: int, logits: torch.Tensor | None = None, counts: torch.Tensor | None = None,
                           offsets: torch.Tensor | None = None, entries: torch.Tensor | None = None,
                           stream=None) -> None:
@@ -191,6 +220,15 @@ class MoeFfn:
         if out is None:
             out = torch.empty_like(x)
         moe_ffn_forward(self.handle, x, out, router_out, router_idx, stream)
+        return out
+
+    def set_norm(self, norm_w, eps: float, stream=None) -> None:
+        moe_ffn_set_norm(self.handle, norm_w, eps, stream)
+
+    def forward_block(self, hidden, out=None, router_out=None, router_idx=None, stream=None):
+        if out is None:
+            out = torch.empty_like(hidden)
+        moe_ffn_forward_block(self.handle, hidden, out, router_out, router_idx, stream)
         return out
 
     def close(self) -> None:

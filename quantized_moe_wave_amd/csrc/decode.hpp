@@ -403,7 +403,7 @@ constexpr int kDcMaxUnits = 2;     // (slot, super-block) units a wave holds in 
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     const uint8_t *__restrict__ Wd, int ngroups, int nsb, const double *__restrict__ logits, int E, int T, int k,
     const float *__restrict__ h, int I, const int32_t *__restrict__ dsel, const float *__restrict__ dw,
-    float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
+    const float *__restrict__ resid, float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ entries, int32_t *__restrict__ pos) {
     const int rg = blockIdx.x, t = blockIdx.y;
@@ -515,7 +515,10 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
             for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][lane & 15];
             o += __shfl(my_w, j, kWave) * y;
         }
-        if (lane < 16) out[(size_t)t * H + rg * kRowGroup + lane] = o;
+        if (lane < 16) {
+            const size_t oi = (size_t)t * H + rg * kRowGroup + lane;
+            out[oi] = resid ? resid[oi] + o : o;  // resid: the block's residual add
+        }
     }
 }
 

@@ -155,7 +155,7 @@ __device__ __forceinline__ uint32_t byte_of(const uint32_t w[2], int j) { return
 // order, no atomics). Grid (ceil(H/1024), T), 256 threads x 4 columns.
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ Y, const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int H, int k,
-                                                      float *__restrict__ out) {
+                                                      const float *__restrict__ resid, float *__restrict__ out) {
     const int t = blockIdx.y;
     const int c = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (c >= H) return;
@@ -167,6 +167,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         acc.y += wj * y.y;
         acc.z += wj * y.z;
         acc.w += wj * y.w;
+    }
+    if (resid) {  // the block's residual add: out = resid + (weighted sum)
+        const float4 r = *(const float4 *)(resid + (size_t)t * H + c);
+        acc.x = r.x + acc.x;
+        acc.y = r.y + acc.y;
+        acc.z = r.z + acc.z;
+        acc.w = r.w + acc.w;
     }
     *(float4 *)(out + (size_t)t * H + c) = acc;
 }

@@ -10,6 +10,9 @@
 //   5. stage_kernel    h rows -> staged
 //   6. expert DOWN     down Q4_K MFMA -> Y[slot][H]
 //   7. combine_kernel  out[t] = sum_j w[t][j] * Y[pos[t][j]]
+// forward_block(T) first runs rmsnorm_kernel (hidden -> normalised rows in the
+// workspace), then the same sequence on those rows, the last kernel adding
+// hidden to its output.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -26,6 +29,7 @@
 #include "decode.hpp"
 #include "expert.hpp"
 #include "gemm.hpp"
+#include "norm.hpp"
 #include "repack.hpp"
 #include "router.hpp"
 #include "stage.hpp"
@@ -79,6 +83,7 @@ struct Workspace {
     f16 *h_xs = nullptr;          // [S][I/256][16]
     float *h_sinv = nullptr;      // [S][I/256]
     float *Y = nullptr;           // [S][H]
+    float *xn = nullptr;          // [T][H] the block's normalised rows (moe_ffn_forward_block)
     int32_t *dsel = nullptr;      // [S] decode path: expert of each (token, slot) pair
     float *dw = nullptr;          // [S] decode path: its renormalised router weight
 };
@@ -101,11 +106,12 @@ enum Stage {
     kStCombine,
     kStGateUpTail,
     kStDownTail,
+    kStNorm,
     kStCount
 };
 const char *const kStageNames[kStCount] = {"router",      "topk",    "bucket",   "stage_x",  "gate_up",
                                            "gate_up_big", "stage_h", "down",     "down_big", "combine",
-                                           "gate_up_tail", "down_tail"};
+                                           "gate_up_tail", "down_tail", "norm"};
 
 // Start/stop events of profiled stages. A profiled kernel is launched with
 // hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
@@ -169,6 +175,8 @@ struct moe_ffn_s {
     uint8_t *dn = nullptr;   // repacked down
     float *rw = nullptr;     // [E][H]
     float *rb = nullptr;     // [E] or null
+    float *norm_w = nullptr; // [H] pre-FFN norm weight (moe_ffn_set_norm), or null
+    float norm_eps = 0.f;
     void *ws_base = nullptr;
     int cap = 0;             // tokens the workspace holds
     Workspace ws;
@@ -244,6 +252,7 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
     w->h_xs = (f16 *)take(S * ni * 16 * 2);
     w->h_sinv = (float *)take(S * ni * 4);
     w->Y = (float *)take(S * H * 4);
+    w->xn = (float *)take(T * H * 4);
     w->dsel = (int32_t *)take(S * 4);
     w->dw = (float *)take(S * 4);
     return off;
@@ -288,99 +297,9 @@ void launch_router(moe_ffn_t h, int T, const float *x, int32_t *idx, float *w, h
            s.num_experts, s.num_experts_per_tok, h->ws.logits, idx, w, h->ws.rcount);
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t moe_ffn_abi_version(void) { return MOE_FFN_ABI_VERSION; }
-
-const char *moe_ffn_last_error(void) { return g_err.c_str(); }
-
-moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size_t gate_bytes, const void *up_q4k,
-                          size_t up_bytes, const void *down_q4k, size_t down_bytes, const float *router_w,
-                          const float *router_bias, void *stream, moe_ffn_t *out) {
-    g_err.clear();
-    if (!out) return fail(MOE_ERR_INVALID_ARG, "out handle pointer is NULL");
-    *out = nullptr;
-    moe_status st = check_shape(shape);
-    if (st != MOE_OK) return st;
-    const moe_ffn_shape s = *shape;
-    const size_t gb = gate_bytes_of(s), db = down_bytes_of(s);
-    if (gate_bytes != gb || up_bytes != gb || down_bytes != db)
-        return fail(MOE_ERR_BLOB_SIZE, "blob sizes gate=%zu up=%zu down=%zu, shape needs gate=up=%zu down=%zu",
-                    gate_bytes, up_bytes, down_bytes, gb, db);
-    if (!gate_q4k || !up_q4k || !down_q4k || !router_w)
-        return fail(MOE_ERR_INVALID_ARG, "gate, up, down and router_w must not be NULL");
-    if (!is_device_ptr(gate_q4k) || !is_device_ptr(up_q4k) || !is_device_ptr(down_q4k) || !is_device_ptr(router_w) ||
-        (router_bias && !is_device_ptr(router_bias)))
-        return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
-    hipStream_t hs = (hipStream_t)stream;
-    {
-        const hipError_t a[6] = {
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds)};
-        for (hipError_t e : a)
-            if (e != hipSuccess)
-                return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
-                            GemmShape<4, 4, 8>::Lds, hipGetErrorString(e));
-    }
-    moe_ffn_t h = new moe_ffn_s();
-    h->sh = s;
-    auto cleanup = [&](moe_status r) {
-        moe_ffn_destroy(h);
-        return r;
-    };
-    if (hipGetDevice(&h->device) != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "hipGetDevice failed"));
-    {
-        // the big GEMMs' tail split assumes workgroups spread round-robin over 8 XCDs of equal size
-        hipDeviceProp_t prop;
-        if (hipGetDeviceProperties(&prop, h->device) != hipSuccess)
-            return cleanup(fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed"));
-        h->cus_per_xcd = prop.multiProcessorCount % 8 == 0 ? prop.multiProcessorCount / 8 : 0;
-    }
-    const int E = s.num_experts, H = s.hidden_dim, I = s.moe_intermediate;
-    if (hipMalloc(&h->gu, 2 * gb) != hipSuccess || hipMalloc(&h->dn, db) != hipSuccess ||
-        hipMalloc(&h->rw, (size_t)E * H * 4) != hipSuccess ||
-        (router_bias && hipMalloc(&h->rb, (size_t)E * 4) != hipSuccess))
-        return cleanup(fail(MOE_ERR_OOM, "weight allocation failed (%zu bytes)", 2 * gb + db));
-    hipError_t e = hipMemcpyAsync(h->rw, router_w, (size_t)E * H * 4, hipMemcpyDeviceToDevice, hs);
-    if (e == hipSuccess && router_bias) e = hipMemcpyAsync(h->rb, router_bias, (size_t)E * 4, hipMemcpyDeviceToDevice, hs);
-    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "router copy failed: %s", hipGetErrorString(e)));
-    const int nh = H / kQ4Weights, ni = I / kQ4Weights;
-    auto rep = [&](const void *src, uint8_t *dst, int rows, int nsb, int kind) {
-        const long total = (long)E * rows * nsb;
-        repack_kernel<<<(unsigned)((total + 255) / 256), 256, 0, hs>>>((const uint8_t *)src, dst, E, rows, nsb, kind);
-    };
-    rep(gate_q4k, h->gu, I, nh, 0);
-    rep(up_q4k, h->gu, I, nh, 1);
-    rep(down_q4k, h->dn, H, ni, 2);
-    e = hipGetLastError();
-    if (e == hipSuccess) e = hipStreamSynchronize(hs);
-    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "weight repack failed: %s", hipGetErrorString(e)));
-    *out = h;
-    return MOE_OK;
-}
-
-moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream) {
-    g_err.clear();
-    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
-    if (max_tokens < 1) return fail(MOE_ERR_INVALID_SHAPE, "max_tokens must be >= 1 (got %d)", max_tokens);
-    return ensure_ws(h, max_tokens, (hipStream_t)stream);
-}
-
-moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
-                           int32_t *router_idx, void *stream) {
-    g_err.clear();
+// Argument checks shared by the forward entry points (x is the layer's input,
+// or the block's residual stream).
+moe_status check_call(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out, int32_t *router_idx) {
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
     if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "token count must be >= 1 (got %d)", T);
     const moe_ffn_shape &s = h->sh;
@@ -400,7 +319,15 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     if (router_idx && (overlaps(router_idx, kb, x, xb) || overlaps(router_idx, kb, out, xb) ||
                        (router_out && overlaps(router_idx, kb, router_out, kb))))
         return fail(MOE_ERR_INVALID_ARG, "router_idx overlaps another buffer");
-    hipStream_t st = (hipStream_t)stream;
+    return MOE_OK;
+}
+
+// The layer on T tokens of x (already checked); resid, if not null, is added
+// to the output by the kernel that writes it (the block's residual add).
+moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out, int32_t *router_idx,
+                         const float *resid, hipStream_t st) {
+    const moe_ffn_shape &s = h->sh;
+    const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
     moe_status r = ensure_ws(h, T, st);
     if (r != MOE_OK) return r;
     Workspace &w = h->ws;
@@ -417,7 +344,7 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
         launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
-               H / kRowGroup, ni, w.logits, E, T, k, w.h, I, w.dsel, w.dw, out, H, idx, wt, w.counts, w.offsets,
+               H / kRowGroup, ni, w.logits, E, T, k, w.h, I, w.dsel, w.dw, resid, out, H, idx, wt, w.counts, w.offsets,
                w.entries, w.pos);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
@@ -514,12 +441,145 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
         }
     }
 
-    launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, out);
+    launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, resid, out);
 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_T = T;
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_ffn_abi_version(void) { return MOE_FFN_ABI_VERSION; }
+
+const char *moe_ffn_last_error(void) { return g_err.c_str(); }
+
+moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size_t gate_bytes, const void *up_q4k,
+                          size_t up_bytes, const void *down_q4k, size_t down_bytes, const float *router_w,
+                          const float *router_bias, void *stream, moe_ffn_t *out) {
+    g_err.clear();
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out handle pointer is NULL");
+    *out = nullptr;
+    moe_status st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    const moe_ffn_shape s = *shape;
+    const size_t gb = gate_bytes_of(s), db = down_bytes_of(s);
+    if (gate_bytes != gb || up_bytes != gb || down_bytes != db)
+        return fail(MOE_ERR_BLOB_SIZE, "blob sizes gate=%zu up=%zu down=%zu, shape needs gate=up=%zu down=%zu",
+                    gate_bytes, up_bytes, down_bytes, gb, db);
+    if (!gate_q4k || !up_q4k || !down_q4k || !router_w)
+        return fail(MOE_ERR_INVALID_ARG, "gate, up, down and router_w must not be NULL");
+    if (!is_device_ptr(gate_q4k) || !is_device_ptr(up_q4k) || !is_device_ptr(down_q4k) || !is_device_ptr(router_w) ||
+        (router_bias && !is_device_ptr(router_bias)))
+        return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
+    hipStream_t hs = (hipStream_t)stream;
+    {
+        const hipError_t a[6] = {
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds),
+            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds)};
+        for (hipError_t e : a)
+            if (e != hipSuccess)
+                return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
+                            GemmShape<4, 4, 8>::Lds, hipGetErrorString(e));
+    }
+    moe_ffn_t h = new moe_ffn_s();
+    h->sh = s;
+    auto cleanup = [&](moe_status r) {
+        moe_ffn_destroy(h);
+        return r;
+    };
+    if (hipGetDevice(&h->device) != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "hipGetDevice failed"));
+    {
+        // the big GEMMs' tail split assumes workgroups spread round-robin over 8 XCDs of equal size
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, h->device) != hipSuccess)
+            return cleanup(fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed"));
+        h->cus_per_xcd = prop.multiProcessorCount % 8 == 0 ? prop.multiProcessorCount / 8 : 0;
+    }
+    const int E = s.num_experts, H = s.hidden_dim, I = s.moe_intermediate;
+    if (hipMalloc(&h->gu, 2 * gb) != hipSuccess || hipMalloc(&h->dn, db) != hipSuccess ||
+        hipMalloc(&h->rw, (size_t)E * H * 4) != hipSuccess ||
+        (router_bias && hipMalloc(&h->rb, (size_t)E * 4) != hipSuccess))
+        return cleanup(fail(MOE_ERR_OOM, "weight allocation failed (%zu bytes)", 2 * gb + db));
+    hipError_t e = hipMemcpyAsync(h->rw, router_w, (size_t)E * H * 4, hipMemcpyDeviceToDevice, hs);
+    if (e == hipSuccess && router_bias) e = hipMemcpyAsync(h->rb, router_bias, (size_t)E * 4, hipMemcpyDeviceToDevice, hs);
+    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "router copy failed: %s", hipGetErrorString(e)));
+    const int nh = H / kQ4Weights, ni = I / kQ4Weights;
+    auto rep = [&](const void *src, uint8_t *dst, int rows, int nsb, int kind) {
+        const long total = (long)E * rows * nsb;
+        repack_kernel<<<(unsigned)((total + 255) / 256), 256, 0, hs>>>((const uint8_t *)src, dst, E, rows, nsb, kind);
+    };
+    rep(gate_q4k, h->gu, I, nh, 0);
+    rep(up_q4k, h->gu, I, nh, 1);
+    rep(down_q4k, h->dn, H, ni, 2);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return cleanup(fail(MOE_ERR_DEVICE, "weight repack failed: %s", hipGetErrorString(e)));
+    *out = h;
+    return MOE_OK;
+}
+
+moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (max_tokens < 1) return fail(MOE_ERR_INVALID_SHAPE, "max_tokens must be >= 1 (got %d)", max_tokens);
+    return ensure_ws(h, max_tokens, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                           int32_t *router_idx, void *stream) {
+    g_err.clear();
+    moe_status r = check_call(h, T, x, out, router_out, router_idx);
+    if (r != MOE_OK) return r;
+    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (!norm_w) return fail(MOE_ERR_INVALID_ARG, "norm_w must not be NULL");
+    if (!(eps >= 0.f) || !(eps < INFINITY)) return fail(MOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    hipStream_t st = (hipStream_t)stream;
+    const size_t bytes = (size_t)h->sh.hidden_dim * 4;
+    if (!h->norm_w) {
+        void *p = nullptr;
+        if (hipMalloc(&p, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(MOE_ERR_OOM, "could not allocate %zu bytes for the norm weight", bytes);
+        }
+        h->norm_w = (float *)p;
+    }
+    HIP_TRY(hipMemcpyAsync(h->norm_w, norm_w, bytes, hipMemcpyDefault, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    h->norm_eps = eps;
+    return MOE_OK;
+}
+
+moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, float *out, float *router_out,
+                                 int32_t *router_idx, void *stream) {
+    g_err.clear();
+    moe_status r = check_call(h, T, hidden, out, router_out, router_idx);
+    if (r != MOE_OK) return r;
+    if (!h->norm_w) return fail(MOE_ERR_INVALID_ARG, "no norm weight on this handle (call moe_ffn_set_norm first)");
+    hipStream_t st = (hipStream_t)stream;
+    r = ensure_ws(h, T, st);
+    if (r != MOE_OK) return r;
+    launch(h->prof, kStNorm, rmsnorm_kernel, dim3(T), dim3(256), st, hidden, h->norm_w, h->sh.hidden_dim,
+           (double)h->norm_eps, h->ws.xn);
+    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, st);
 }
 
 moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets, int32_t *entries,
@@ -575,6 +635,7 @@ moe_status moe_ffn_destroy(moe_ffn_t h) {
     if (h->dn) (void)hipFree(h->dn);
     if (h->rw) (void)hipFree(h->rw);
     if (h->rb) (void)hipFree(h->rb);
+    if (h->norm_w) (void)hipFree(h->norm_w);
     if (h->ws_base) (void)hipFree(h->ws_base);
     delete h;
     return MOE_OK;

@@ -64,7 +64,8 @@ def make_layer(inp: synth.LayerInputs, dev_inputs=None):
     return layer, d
 
 
-def run_gpu(layer, x_dev) -> GpuRun:
+def run_gpu(layer, x_dev, block: bool = False) -> GpuRun:
+    """One forward (block: forward_block, x_dev then being the residual stream) and its routing state."""
     import torch
 
     import quantized_moe_wave_amd as q
@@ -74,7 +75,10 @@ def run_gpu(layer, x_dev) -> GpuRun:
     out = torch.empty_like(x_dev)
     w = torch.empty((T, k), dtype=torch.float32, device=x_dev.device)
     idx = torch.empty((T, k), dtype=torch.int32, device=x_dev.device)
-    layer.forward(x_dev, out, w, idx)
+    if block:
+        layer.forward_block(x_dev, out, w, idx)
+    else:
+        layer.forward(x_dev, out, w, idx)
     logits = torch.empty((T, E), dtype=torch.float64, device=x_dev.device)
     counts = torch.empty(E, dtype=torch.int32, device=x_dev.device)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=x_dev.device)
@@ -102,8 +106,9 @@ def out_errors(gpu: np.ndarray, ref: np.ndarray):
     return float(max_rel), float(l1_rel)
 
 
-def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None):
-    """Assert the bar. sel: token subset for the expert part (None = all)."""
+def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None, resid=None):
+    """Assert the bar. sel: token subset for the expert part (None = all). resid: the block's residual stream
+    [T][H] (inp.x then holds the normalised rows the layer ran on); the reference output is resid + layer."""
     k, E = inp.wl.top_k, inp.wl.experts
     ref = oracle.forward(inp.x, inp.router, inp.bias, inp.gate, inp.up, inp.down, k, sel=sel)
     T = inp.x.shape[0]
@@ -143,6 +148,8 @@ def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None):
         forced = oracle.forward(inp.x, inp.router, inp.bias, inp.gate, inp.up, inp.down, k, sel=tokens[td],
                                 idx_in=g.idx)
         ref_out[td] = forced["out"]
+    if resid is not None:
+        ref_out = oracle.add_residual(np.ascontiguousarray(resid[tokens]), ref_out)
     max_rel, l1_rel = out_errors(g.out[tokens], ref_out)
     if report is not None:
         report.update(dict(logit_err=logit_err, max_rel=max_rel, l1_rel=l1_rel, ties=int(ties.sum()),
