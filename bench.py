@@ -20,6 +20,9 @@ Single eager steps (median, 10th / 90th percentile) go under "step_us": "warm" w
 only a GPU sleep between steps, "cold" with a 512 MB write between steps (outside
 the timed events) that leaves no weight or input in any cache.
 
+The layer inside its block (moe_ffn_forward_block: pre-FFN RMSNorm, the layer, residual
+add) is timed the same way on the decode and prefill workloads under "block".
+
 The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
 For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
 (the decode kernels' weight bytes) the same way.
@@ -61,6 +64,7 @@ def parse_args():
     ap.add_argument("--prefill-workload", default="30b-prefill")
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-block", action="store_true", help="skip timing the layer inside its block")
     ap.add_argument("--extra-workloads", default="30b-batch,235b-shape",
                     help="comma-separated workloads whose whole-step time is reported under \"others\" ('' for none)")
     ap.add_argument("--extra-steps", type=int, default=50)
@@ -76,13 +80,14 @@ def parse_args():
 class Bench:
     """R replicas of one workload on the GPU, with their outputs preallocated."""
 
-    def __init__(self, wl, replicas: int, seed: int = 1):
+    def __init__(self, wl, replicas: int, seed: int = 1, block: bool = False):
         import torch
 
         import synth
         from tests import parity
 
         self.wl = wl
+        self.block = block
         self.layers, self.xs, self.outs, self.ws, self.idxs = [], [], [], [], []
         self.host0 = None
         for r in range(replicas):
@@ -91,6 +96,8 @@ class Bench:
             dev = parity.upload(inp)
             layer, _ = parity.make_layer(inp, dev)
             layer.reserve(wl.tokens)
+            if block:
+                layer.set_norm(torch.from_numpy(synth.gen_norm(seed, r, wl.hidden)), synth.NORM_EPS)
             x = dev["x"]
             for key in ("gate", "up", "down", "router", "bias"):
                 dev[key] = None  # the layer owns its copies
@@ -109,7 +116,10 @@ class Bench:
 
     def step(self, i: int) -> None:
         r = i % self.R
-        self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+        if self.block:
+            self.layers[r].forward_block(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+        else:
+            self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
 
     def routing(self):
         """Per replica: (distinct experts U, max tokens on one expert, rows in GEMM buckets)."""
@@ -350,6 +360,26 @@ def measure_step(wl, steps: int, eager: bool, want_stages: bool = False) -> dict
                           "frac": round(flops / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
 
 
+def measure_block(wl, steps: int, eager: bool) -> dict:
+    """The layer inside its block (moe_ffn_forward_block: RMSNorm, the layer, residual add), timed like the main
+    step, with the norm kernel's own time from kernel-stamped events."""
+    import torch
+
+    b = Bench(wl, replicas_for(wl), block=True)
+    try:
+        ms = b.timed(steps, max(3, steps // 10), eager)
+        st = b.stage_times(steps, ["norm"])["norm"]
+        n = sum(p[2] for p in st)
+        norm_us = sum(p[1] for p in st) / max(n, 1) * 1e3
+    finally:
+        b.close()
+        del b
+        torch.cuda.empty_cache()
+    log(f"{wl.name} block: {ms * 1e3:.2f} us/step, norm kernel {norm_us:.2f} us")
+    return {"workload": wl.name, "tokens": wl.tokens, "steps": steps, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "norm_kernel_us": round(norm_us, 3)}
+
+
 def cpu_baseline(inp, seconds: float):
     """The oracle on T=1 forwards of replica 0's weights, one token per call, for ~seconds."""
     import numpy as np
@@ -481,6 +511,10 @@ def main() -> int:
             "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
             "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof, "step_us": pdist,
         }
+    if not args.no_block:
+        line["block"] = [measure_block(wl, args.steps, args.eager)]
+        if not args.no_prefill:
+            line["block"].append(measure_block(synth.WORKLOADS[args.prefill_workload], args.prefill_steps, args.eager))
     line["hbm_step"]["plain_copy_probe"] = copy_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]
     if extras:

@@ -24,6 +24,7 @@
 #pragma once
 #include "common.hpp"
 #include "expert.hpp"
+#include "norm.hpp"
 #include "router.hpp"
 #include "stage.hpp"
 
@@ -53,10 +54,14 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
 // One wave per expert (waves 0 .. E-1 of the grid) and one per (token,
 // super-block) staging unit of x (the T*nsb waves after them), so that no
 // wave does both one after the other.
+// norm_w (the block's RMSNorm weight, or null): x holds the residual stream
+// and every value is used normalised, fp32(x * norm_w * inv_rms), each wave
+// computing the 1/rms of the rows it reads (row_inv_rms).
 __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, const float *__restrict__ wr,
                                                   const float *__restrict__ bias, int T, int H, int E,
                                                   double *__restrict__ logits, f16 *__restrict__ x_hilo,
-                                                  f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
+                                                  f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
+                                                  const float *__restrict__ norm_w, double eps) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nsb = H / kQ4Weights;
     const int wpb = blockDim.x >> 6;  // waves per workgroup
@@ -65,8 +70,9 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
     for (int u = blockIdx.x * wpb + wave - E; u < T * nsb; u += nw) {
         if (u < 0) break;  // an expert wave
         const int t = u / nsb, b = u % nsb;
+        const double ir = norm_w ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
         stage_row_sb(x + (size_t)t * H, nsb, b, x_hilo + (size_t)t * 2 * H, x_xs + (size_t)t * nsb * 16,
-                     x_sinv + (size_t)t * nsb);
+                     x_sinv + (size_t)t * nsb, -10000, norm_w, ir);
     }
 
     // Loads are unconditional (chunk and token indices clamped) so that all of
@@ -75,6 +81,12 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
         double acc[kSmallT];
 #pragma unroll
         for (int t = 0; t < kSmallT; ++t) acc[t] = 0.0;
+        // 1/rms of each token's row: from the chunk registers below when the
+        // whole row fits one pass of them (nsb <= 8), else read ahead here
+        const bool rms_ahead = norm_w && nsb > 8;
+        double ir[kSmallT];
+#pragma unroll
+        for (int t = 0; t < kSmallT; ++t) ir[t] = (rms_ahead && t < T) ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
         const float *wrow = wr + (size_t)e * H;
         for (int c0 = 0; c0 < nsb; c0 += 8) {
             float4 wv[8], xv[kSmallT][8];
@@ -86,6 +98,41 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                 for (int i = 0; i < 8; ++i)
                     xv[t][i] = *(const float4 *)(x + (size_t)min(t, T - 1) * H + min(c0 + i, nsb - 1) * kQ4Weights +
                                                  lane * 4);
+            if (norm_w) {
+                float4 gv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) gv[i] = *(const float4 *)(norm_w + min(c0 + i, nsb - 1) * kQ4Weights + lane * 4);
+                if (!rms_ahead) {
+#pragma unroll
+                    for (int t = 0; t < kSmallT; ++t) {
+                        if (t < T) {
+                            double ss = 0.0;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) {
+                                if (i < nsb) {
+                                    ss += (double)xv[t][i].x * xv[t][i].x;
+                                    ss += (double)xv[t][i].y * xv[t][i].y;
+                                    ss += (double)xv[t][i].z * xv[t][i].z;
+                                    ss += (double)xv[t][i].w * xv[t][i].w;
+                                }
+                            }
+                            ir[t] = 1.0 / sqrt(wave_sum(ss) / (double)H + eps);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                    for (int t = 0; t < kSmallT; ++t) {
+                        if (t >= T) continue;
+                        const float4 g4 = gv[i];
+                        xv[t][i].x = (float)((double)xv[t][i].x * g4.x * ir[t]);
+                        xv[t][i].y = (float)((double)xv[t][i].y * g4.y * ir[t]);
+                        xv[t][i].z = (float)((double)xv[t][i].z * g4.z * ir[t]);
+                        xv[t][i].w = (float)((double)xv[t][i].w * g4.w * ir[t]);
+                    }
+                }
+            }
 #pragma unroll
             for (int t = 0; t < kSmallT; ++t) {
 #pragma unroll
@@ -242,8 +289,9 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
 __global__ __launch_bounds__(64) void router_small_kernel(const float *__restrict__ x, const float *__restrict__ wr,
                                                            const float *__restrict__ bias, int T, int H, int E,
                                                            double *__restrict__ logits, f16 *__restrict__ x_hilo,
-                                                           f16 *__restrict__ x_xs, float *__restrict__ x_sinv) {
-    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv);
+                                                           f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
+                                                           const float *__restrict__ norm_w, double eps) {
+    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv, norm_w, eps);
 }
 
 constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS

@@ -12,7 +12,8 @@
 //   7. combine_kernel  out[t] = sum_j w[t][j] * Y[pos[t][j]]
 // forward_block(T) first runs rmsnorm_kernel (hidden -> normalised rows in the
 // workspace), then the same sequence on those rows, the last kernel adding
-// hidden to its output.
+// hidden to its output; on the decode path the router launch normalises the
+// values it reads instead (no norm launch).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -322,10 +323,19 @@ moe_status check_call(moe_ffn_t h, int32_t T, const float *x, float *out, float 
     return MOE_OK;
 }
 
+// Whether T tokens take the decode path (decode.hpp): few tokens, and shapes
+// whose staged row, ranking and per-token down units fit its kernels.
+bool decode_path(const moe_ffn_shape &s, int T) {
+    const int H = s.hidden_dim, E = s.num_experts, k = s.num_experts_per_tok, ni = s.moe_intermediate / kQ4Weights;
+    return T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6;
+}
+
 // The layer on T tokens of x (already checked); resid, if not null, is added
 // to the output by the kernel that writes it (the block's residual add).
+// norm_w (decode path only): x is the residual stream and the router launch
+// applies the block's RMSNorm (weight norm_w, eps) to every value it reads.
 moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out, int32_t *router_idx,
-                         const float *resid, hipStream_t st) {
+                         const float *resid, const float *norm_w, double eps, hipStream_t st) {
     const moe_ffn_shape &s = h->sh;
     const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
     moe_status r = ensure_ws(h, T, st);
@@ -337,10 +347,11 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
     Profiler &pf = h->prof;
-    if (T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6) {
+    if (norm_w && !decode_path(s, T)) return fail(MOE_ERR_INVALID_ARG, "internal: fused norm off the decode path");
+    if (decode_path(s, T)) {
         // decode path: three launches (see decode.hpp)
         launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
-               w.logits, w.x_hilo, w.x_xs, w.x_sinv);
+               w.logits, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
         launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
@@ -544,7 +555,7 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     g_err.clear();
     moe_status r = check_call(h, T, x, out, router_out, router_idx);
     if (r != MOE_OK) return r;
-    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, (hipStream_t)stream);
+    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, (hipStream_t)stream);
 }
 
 moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *stream) {
@@ -575,11 +586,14 @@ moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, fl
     if (r != MOE_OK) return r;
     if (!h->norm_w) return fail(MOE_ERR_INVALID_ARG, "no norm weight on this handle (call moe_ffn_set_norm first)");
     hipStream_t st = (hipStream_t)stream;
+    // decode path: the norm is fused into its router launch
+    if (decode_path(h->sh, T))
+        return forward_layer(h, T, hidden, out, router_out, router_idx, hidden, h->norm_w, (double)h->norm_eps, st);
     r = ensure_ws(h, T, st);
     if (r != MOE_OK) return r;
     launch(h->prof, kStNorm, rmsnorm_kernel, dim3(T), dim3(256), st, hidden, h->norm_w, h->sh.hidden_dim,
            (double)h->norm_eps, h->ws.xn);
-    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, st);
+    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, nullptr, 0.0, st);
 }
 
 moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets, int32_t *entries,

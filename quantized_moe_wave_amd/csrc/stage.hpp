@@ -29,9 +29,12 @@ __device__ __forceinline__ int stage_exponent(float m) {
 // One wave stages super-block b of one row with scale 2^se (se < -1000: use
 // the block's own scale): src points at the row's fp32 values (K = nsb*256
 // columns); lanes 0..31 each own one 8-column fragment.
+// With nw (the block's RMSNorm weight, or null) the staged values are the
+// normalised row: fp32(src[c] * nw[c] * inv_rms), the product in double.
 __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int nsb, int b, f16 *__restrict__ hilo_row,
                                              f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
-                                             int se = -10000) {
+                                             int se = -10000, const float *__restrict__ nw = nullptr,
+                                             double inv_rms = 1.0) {
     const int lane = threadIdx.x & 63;
     const int f = lane & 31;  // fragment: k-step s = f / 4, lane group g = f % 4
     const int s = f >> 2, g = f & 3;
@@ -42,6 +45,14 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
         float4 c = *(const float4 *)(p + 4);
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+    }
+    if (nw) {
+        const float *q = nw + b * kQ4Weights + s * 32 + g * 8;
+        const float4 a = *(const float4 *)q;
+        const float4 c = *(const float4 *)(q + 4);
+        const float w[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (float)((double)v[i] * w[i] * inv_rms);
     }
     if (se < -1000) {
         float m = 0.f;
