@@ -63,6 +63,7 @@ def load():
     lib.mo_forward.restype = ctypes.c_int
     lib.mo_rms_norm.argtypes = [i32, i32, vp, vp, f64, vp]
     lib.mo_add_residual.argtypes = [i64, vp, vp, vp]
+    lib.mo_stage_stats.argtypes = [i64, vp, vp]
     _lib = lib
     return lib
 
@@ -232,3 +233,14 @@ def block(hidden, norm_w, eps: float, router_w, bias, gate, up, down, k: int, se
     r["out"] = add_residual(rows, r["out"])
     r["xn"] = xn
     return r
+
+
+STAT_FIELDS = ("n", "nan", "inf", "min", "max", "mean", "rms")
+
+
+def stage_stats(v) -> np.ndarray:
+    """Statistics of one stage's values (any shape, widened to float64): the 7 fields of STAT_FIELDS."""
+    v = np.ascontiguousarray(np.asarray(v, np.float64).ravel())
+    s = np.empty(7, np.float64)
+    load().mo_stage_stats(v.size, _ptr(v), _ptr(s))
+    return s

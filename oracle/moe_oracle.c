@@ -374,3 +374,38 @@ void mo_rms_norm(int32_t T, int32_t H, const float *x, const float *g, double ep
 void mo_add_residual(int64_t n, const float *hidden, const double *ffn, double *out) {
     for (int64_t i = 0; i < n; ++i) out[i] = (double)hidden[i] + ffn[i];
 }
+
+/* ------------------------------------------------------ per-stage statistics */
+
+/* Statistics of one stage's values, the traced forward's per-stage summary
+ * (forward_qwen3_moe_cuda_traced.rs: per-layer activation statistics of the
+ * last token, used to find the first stage where a NaN or Inf enters; the page
+ * names the statistics type but not its fields). Fields taken:
+ *   s[0] number of values, s[1] NaN count, s[2] +-Inf count, and over the
+ *   finite values only: s[3] min, s[4] max, s[5] mean, s[6] root mean square
+ *   (all four 0 when no value is finite). */
+void mo_stage_stats(int64_t n, const double *v, double s[7]) {
+    int64_t nan = 0, inf = 0, fin = 0;
+    double mn = 0.0, mx = 0.0, sum = 0.0, sq = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double x = v[i];
+        if (x != x) {
+            ++nan;
+        } else if (x == INFINITY || x == -INFINITY) {
+            ++inf;
+        } else {
+            if (fin == 0 || x < mn) mn = x;
+            if (fin == 0 || x > mx) mx = x;
+            sum += x;
+            sq += x * x;
+            ++fin;
+        }
+    }
+    s[0] = (double)n;
+    s[1] = (double)nan;
+    s[2] = (double)inf;
+    s[3] = mn;
+    s[4] = mx;
+    s[5] = fin ? sum / (double)fin : 0.0;
+    s[6] = fin ? sqrt(sq / (double)fin) : 0.0;
+}
