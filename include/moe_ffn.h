@@ -155,6 +155,31 @@ moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, fl
 moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets,
                                  int32_t *entries, void *stream);
 
+/* Per-stage statistics of one token of the most recent forward on this handle
+ * (moe_ffn_forward or moe_ffn_forward_block): the traced forward's summary
+ * (forward_qwen3_moe_cuda_traced.rs, doc of forward_qwen3_moe_cuda_traced:
+ * per-layer activation statistics of the last token, with its MoeRouter and
+ * MoeFfnOut stages, used to find the first stage where a NaN or Inf enters).
+ *   token       0 <= token < T of that forward (the pages' traced path takes
+ *               the last).
+ *   out         the [T][H] output buffer that forward wrote.
+ *   router_out  the router_out that forward was given (NULL if it was NULL).
+ *   stats       [4][7] fp64 device array. Stages: 0 router logits (E values,
+ *               bias included), 1 router weights (k, MoeRouter), 2 SwiGLU
+ *               output h of the token's k slots (k * moe_intermediate values,
+ *               slot order), 3 the output row (hidden_dim values: MoeFfnOut,
+ *               or the block output). Fields: number of values, NaN count,
+ *               +-Inf count, then over the finite values min, max, mean and
+ *               root mean square (each 0 when no value is finite). The page
+ *               names the statistics type without its fields; these are the
+ *               reading taken.
+ * Enqueued on stream after the forward; reads the workspace, so no other
+ * forward may run on the handle in between.
+ * Errors: INVALID_ARG (bad handle, no forward yet, token out of range, host
+ * pointers), DEVICE. */
+moe_status moe_ffn_debug_stats(moe_ffn_t h, int32_t token, const float *out, const float *router_out,
+                               double *stats, void *stream);
+
 /* Per-stage GPU timing for benchmarks. Stages of one forward, in launch order:
  * 0 router (logits, and for at most 4 tokens also the top-k), 1 topk (which
  * also stages x when num_experts <= 256), 2 bucket, 3 stage_x (when the top-k

@@ -5,10 +5,13 @@ include/moe_ffn.h; this package is a thin ctypes binding with the same names.
 """
 from .binding import (  # noqa: F401
     MoeError,
+    STAT_FIELDS,
+    STAT_STAGES,
     MoeFfn,
     abi_version,
     moe_ffn_create,
     moe_ffn_debug_routing,
+    moe_ffn_debug_stats,
     moe_ffn_destroy,
     moe_ffn_forward,
     moe_ffn_forward_block,

@@ -42,6 +42,8 @@ _lib.moe_ffn_set_norm.argtypes = [_vp, _vp, ctypes.c_float, _vp]
 _lib.moe_ffn_set_norm.restype = ctypes.c_int
 _lib.moe_ffn_forward_block.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_forward_block.restype = ctypes.c_int
+_lib.moe_ffn_debug_stats.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_debug_stats.restype = ctypes.c_int
 _lib.moe_ffn_debug_routing.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_debug_routing.restype = ctypes.c_int
 _lib.moe_ffn_destroy.argtypes = [_vp]
@@ -173,6 +175,28 @@ def moe_ffn_debug_routing(handle: int, logits: torch.Tensor | None = None, count
     st = _lib.moe_ffn_debug_routing(_vp(handle), _ptr(logits), _ptr(counts), _ptr(offsets), _ptr(entries),
                                     _stream(stream))
     _check(st, "moe_ffn_debug_routing")
+
+
+STAT_STAGES = ("router_logits", "router_weights", "swiglu_h", "output")
+STAT_FIELDS = ("n", "nan", "inf", "min", "max", "mean", "rms")
+
+
+def moe_ffn_debug_stats(handle: int, token: int, out: torch.Tensor, router_out: torch.Tensor | None = None,
+                        stats: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Per-stage statistics [4][7] float64 (STAT_STAGES x STAT_FIELDS) of one token of the last forward. out and
+    router_out: the buffers that forward wrote (router_out None if it was given none)."""
+    _dev(out, "out", torch.float32)
+    if router_out is not None:
+        _dev(router_out, "router_out", torch.float32)
+    if stats is None:
+        stats = torch.empty((len(STAT_STAGES), len(STAT_FIELDS)), dtype=torch.float64, device=out.device)
+    _dev(stats, "stats", torch.float64)
+    if stats.numel() < len(STAT_STAGES) * len(STAT_FIELDS):
+        raise ValueError("stats must hold 4 x 7 values")
+    st = _lib.moe_ffn_debug_stats(_vp(handle), int(token), _ptr(out), _ptr(router_out), _ptr(stats),
+                                  _stream(stream))
+    _check(st, "moe_ffn_debug_stats")
+    return stats
 
 
 def moe_ffn_stage_names() -> list[str]:

@@ -34,6 +34,7 @@
 #include "repack.hpp"
 #include "router.hpp"
 #include "stage.hpp"
+#include "stats.hpp"
 
 using namespace moe;
 
@@ -182,6 +183,7 @@ struct moe_ffn_s {
     int cap = 0;             // tokens the workspace holds
     Workspace ws;
     int last_T = 0;
+    bool last_decode = false;  // whether the most recent forward took the decode path (h rows in pair order)
     Profiler prof;
 };
 
@@ -360,6 +362,7 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
         h->last_T = T;
+        h->last_decode = true;
         return MOE_OK;
     }
     bool staged_x = false;
@@ -457,6 +460,7 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_T = T;
+    h->last_decode = false;
     return MOE_OK;
 }
 
@@ -610,6 +614,24 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
     if (counts) HIP_TRY(hipMemcpyAsync(counts, h->ws.counts, E * 4, hipMemcpyDeviceToDevice, st));
     if (offsets) HIP_TRY(hipMemcpyAsync(offsets, h->ws.offsets, (E + 1) * 4, hipMemcpyDeviceToDevice, st));
     if (entries) HIP_TRY(hipMemcpyAsync(entries, h->ws.entries, T * k * 4, hipMemcpyDeviceToDevice, st));
+    return MOE_OK;
+}
+
+moe_status moe_ffn_debug_stats(moe_ffn_t h, int32_t token, const float *out, const float *router_out,
+                               double *stats, void *stream) {
+    g_err.clear();
+    if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
+    if (h->last_T < 1) return fail(MOE_ERR_INVALID_ARG, "no forward has run on this handle");
+    if (token < 0 || token >= h->last_T)
+        return fail(MOE_ERR_INVALID_ARG, "token %d outside the last forward's 0..%d", token, h->last_T - 1);
+    if (!is_device_ptr(out) || !is_device_ptr(stats) || (router_out && !is_device_ptr(router_out)))
+        return fail(MOE_ERR_INVALID_ARG, "out, stats and router_out must be device pointers");
+    const moe_ffn_shape &s = h->sh;
+    hipLaunchKernelGGL(stage_stats_kernel, dim3(kStatStages), dim3(256), 0, (hipStream_t)stream, h->ws.logits,
+                       router_out ? router_out : h->ws.w, h->ws.h, h->last_decode ? nullptr : h->ws.pos, out,
+                       (int)token, s.num_experts, s.num_experts_per_tok, s.moe_intermediate, s.hidden_dim, stats);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     return MOE_OK;
 }
 
