@@ -21,7 +21,8 @@ only a GPU sleep between steps, "cold" with a 512 MB write between steps (outsid
 the timed events) that leaves no weight or input in any cache.
 
 The layer inside its block (moe_ffn_forward_block: pre-FFN RMSNorm, the layer, residual
-add) is timed the same way on the decode and prefill workloads under "block".
+add) is timed the same way on the decode and prefill workloads under "block", with the
+time of one per-stage statistics call (moe_ffn_debug_stats) on the last token.
 
 The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
 For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
@@ -365,19 +366,33 @@ def measure_block(wl, steps: int, eager: bool) -> dict:
     step, with the norm kernel's own time from kernel-stamped events."""
     import torch
 
+    import quantized_moe_wave_amd as q
+
     b = Bench(wl, replicas_for(wl), block=True)
     try:
         ms = b.timed(steps, max(3, steps // 10), eager)
         st = b.stage_times(steps, ["norm"])["norm"]
         n = sum(p[2] for p in st)
         norm_us = sum(p[1] for p in st) / max(n, 1) * 1e3
+        # the per-stage statistics of the last token after a block step (the traced path's summary)
+        b.step(0)
+        stats = torch.empty((4, 7), dtype=torch.float64, device="cuda")
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(200_000)
+        a.record()
+        for _ in range(50):
+            q.moe_ffn_debug_stats(b.layers[0].handle, wl.tokens - 1, b.outs[0], b.ws[0], stats)
+        e.record()
+        torch.cuda.synchronize()
+        stats_us = a.elapsed_time(e) / 50 * 1e3
     finally:
         b.close()
         del b
         torch.cuda.empty_cache()
-    log(f"{wl.name} block: {ms * 1e3:.2f} us/step, norm kernel {norm_us:.2f} us")
+    log(f"{wl.name} block: {ms * 1e3:.2f} us/step, norm kernel {norm_us:.2f} us, stage statistics {stats_us:.2f} us")
     return {"workload": wl.name, "tokens": wl.tokens, "steps": steps, "ms_per_step": round(ms, 5),
-            "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "norm_kernel_us": round(norm_us, 3)}
+            "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "norm_kernel_us": round(norm_us, 3),
+            "stage_stats_us": round(stats_us, 2)}
 
 
 def cpu_baseline(inp, seconds: float):
