@@ -34,8 +34,10 @@ def _block_case(name, T, seed=0, zero_experts=False):
     return inp, hidden, g, run
 
 
+# 235b-shape at T = 2: hidden 4096 (16 super-blocks), where the decode router's logit waves read each token's
+# 1/rms ahead of their chunk loop instead of taking it from the chunk registers
 @pytest.mark.parametrize("name,T", [("tiny", 1), ("tiny", 4), ("tiny", 37), ("30b-decode", 1), ("30b-decode", 3),
-                                    ("30b-batch", 64)])
+                                    ("30b-batch", 64), ("235b-shape", 2)])
 def test_block_parity(name, T):
     print(f"[block] {name} T={T}", flush=True)
     inp, hidden, g, run = _block_case(name, T)
