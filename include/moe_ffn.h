@@ -48,7 +48,8 @@
 extern "C" {
 #endif
 
-#define MOE_FFN_ABI_VERSION 1
+/* 2: adds moe_ffn_set_norm, moe_ffn_forward_block and moe_ffn_debug_stats. */
+#define MOE_FFN_ABI_VERSION 2
 
 typedef struct moe_ffn_s *moe_ffn_t;
 
