@@ -64,6 +64,9 @@ def load():
     lib.mo_rms_norm.argtypes = [i32, i32, vp, vp, f64, vp]
     lib.mo_add_residual.argtypes = [i64, vp, vp, vp]
     lib.mo_stage_stats.argtypes = [i64, vp, vp]
+    lib.mo_q8k_quantize.argtypes = [i64, vp, vp, vp]
+    lib.mo_forward_q8.argtypes = lib.mo_forward.argtypes
+    lib.mo_forward_q8.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -173,11 +176,21 @@ def expert_q4k(x_row: np.ndarray, gate_e: np.ndarray, up_e: np.ndarray, down_e: 
     return y, g, u, h
 
 
-def forward(x, router_w, bias, gate, up, down, k: int, sel=None, idx_in=None):
+def q8k_quantize(v):
+    """Q8_K-style quantisation of fp32 values (length a multiple of 256): (d [n/256] fp32, q [n] int8)."""
+    v = np.ascontiguousarray(np.asarray(v, np.float32).ravel())
+    d = np.empty(v.size // 256, np.float32)
+    q = np.empty(v.size, np.int8)
+    load().mo_q8k_quantize(v.size, _ptr(v), _ptr(d), _ptr(q))
+    return d, q
+
+
+def forward(x, router_w, bias, gate, up, down, k: int, sel=None, idx_in=None, q8: bool = False):
     """Whole layer. Returns dict(out [n_sel][H] f64, idx, w, logits).
 
     sel: optional token list for the expert part (the router runs for all tokens).
     idx_in: optional [T][k] expert choice that replaces the top-k selection.
+    q8: feed the experts' matvecs Q8_K-quantised activations (x rows and h; the router stays fp32).
     """
     x = np.ascontiguousarray(x, np.float32)
     router_w = np.ascontiguousarray(router_w, np.float32)
@@ -195,7 +208,8 @@ def forward(x, router_w, bias, gate, up, down, k: int, sel=None, idx_in=None):
     idx = np.empty((T, k), np.int32)
     wts = np.empty((T, k), np.float64)
     logits = np.empty((T, E), np.float64)
-    rc = load().mo_forward(H, E, k, I, T, _ptr(x), _ptr(router_w), _ptr(bias), _ptr(gate), _ptr(up), _ptr(down),
+    fn = load().mo_forward_q8 if q8 else load().mo_forward
+    rc = fn(H, E, k, I, T, _ptr(x), _ptr(router_w), _ptr(bias), _ptr(gate), _ptr(up), _ptr(down),
                            _ptr(sel_a), n_sel, _ptr(idx_a), _ptr(out), _ptr(idx), _ptr(wts), _ptr(logits))
     if rc != 0:
         raise ValueError("oracle forward rejected its arguments or ran out of memory")

@@ -223,12 +223,64 @@ void mo_bucket(int32_t T, int32_t k, int32_t E, const int32_t *idx, int32_t *cou
 
 double mo_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Q8_K-style activation quantisation (the int8-activation CPU path the
+ * dispatch page compares against, qwen3_moe_dispatch.rs; the pages name it
+ * without its arithmetic, so this reading is taken): per block of 256 fp32
+ * values, amax = max |v|; if amax is 0 then d = 0 and every q = 0, else
+ * q = rint(v * (127 / amax)) (round half to even), clamped to [-127, 127], and
+ * d = amax / 127, with every step in fp32 (the precision that decides the
+ * integer codes). The block then stands for the values d * q. n % 256 == 0. */
+void mo_q8k_quantize(int64_t n, const float *v, float *d, int8_t *q) {
+    for (int64_t b = 0; b < n / 256; ++b) {
+        const float *vb = v + b * 256;
+        float amax = 0.0f;
+        for (int i = 0; i < 256; ++i) {
+            const float a = fabsf(vb[i]);
+            if (a > amax) amax = a;
+        }
+        if (amax == 0.0f) {
+            d[b] = 0.0f;
+            for (int i = 0; i < 256; ++i) q[b * 256 + i] = 0;
+            continue;
+        }
+        const float iscale = 127.0f / amax;
+        for (int i = 0; i < 256; ++i) {
+            float r = rintf(vb[i] * iscale);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            q[b * 256 + i] = (int8_t)r;
+        }
+        d[b] = amax / 127.0f;
+    }
+}
+
+/* x (n fp32 values) replaced by its Q8_K values d * q, in double. */
+static int q8k_round_trip(int64_t n, const float *x, double *out) {
+    float *d = (float *)malloc(sizeof(float) * (size_t)(n / 256));
+    int8_t *q = (int8_t *)malloc((size_t)n);
+    if (!d || !q) {
+        free(d); free(q);
+        return -1;
+    }
+    mo_q8k_quantize(n, x, d, q);
+    for (int64_t i = 0; i < n; ++i) out[i] = (double)d[i / 256] * (double)q[i];
+    free(d); free(q);
+    return 0;
+}
+
 /* One expert on one activation row, with dequantised fp64 matrices
  * Wg, Wu [I][H] and Wd [H][I]:
- *   g = Wg x, u = Wu x, h = SiLU(g) * u, y = Wd h. */
-void mo_expert_dense(int32_t H, int32_t I, const double *Wg, const double *Wu, const double *Wd,
-                     const double *x, double *y, double *g_out, double *u_out, double *h_out) {
+ *   g = Wg x, u = Wu x, h = SiLU(g) * u, y = Wd h.
+ * q8: h enters the down projection as its Q8_K values (h rounded to fp32, then
+ * mo_q8k_quantize), as the int8-activation path feeds each matvec. */
+static int expert_dense_impl(int32_t H, int32_t I, const double *Wg, const double *Wu, const double *Wd,
+                             const double *x, double *y, double *g_out, double *u_out, double *h_out, int q8) {
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    float *hf = q8 ? (float *)malloc(sizeof(float) * (size_t)I) : NULL;
+    if (!h || (q8 && !hf)) {
+        free(h); free(hf);
+        return -1;
+    }
     for (int32_t i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
         for (int32_t c = 0; c < H; ++c) {
@@ -240,12 +292,25 @@ void mo_expert_dense(int32_t H, int32_t I, const double *Wg, const double *Wu, c
         if (u_out) u_out[i] = u;
         if (h_out) h_out[i] = h[i];
     }
+    if (q8) {
+        for (int32_t i = 0; i < I; ++i) hf[i] = (float)h[i];
+        if (q8k_round_trip(I, hf, h) != 0) {
+            free(h); free(hf);
+            return -1;
+        }
+    }
     for (int32_t n = 0; n < H; ++n) {
         double acc = 0.0;
         for (int32_t i = 0; i < I; ++i) acc += Wd[(int64_t)n * I + i] * h[i];
         y[n] = acc;
     }
-    free(h);
+    free(h); free(hf);
+    return 0;
+}
+
+void mo_expert_dense(int32_t H, int32_t I, const double *Wg, const double *Wu, const double *Wd,
+                     const double *x, double *y, double *g_out, double *u_out, double *h_out) {
+    (void)expert_dense_impl(H, I, Wg, Wu, Wd, x, y, g_out, u_out, h_out, 0);
 }
 
 /* Same, straight from one expert's Q4_K blobs (gate/up [I][H/256] blocks,
@@ -280,10 +345,10 @@ int mo_expert_q4k(int32_t H, int32_t I, const uint8_t *gate, const uint8_t *up, 
  * If idx_in is given it replaces the top-k choice (the weights are still the
  * renormalised softmax at those experts); idx_out/w_out/logits_out may be
  * NULL. Returns 0, or -1 on allocation failure / bad arguments. */
-int mo_forward(int32_t H, int32_t E, int32_t k, int32_t I, int32_t T, const float *x, const float *router_w,
-               const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
-               const int32_t *sel, int32_t n_sel, const int32_t *idx_in, double *out, int32_t *idx_out,
-               double *w_out, double *logits_out) {
+static int forward_impl(int32_t H, int32_t E, int32_t k, int32_t I, int32_t T, const float *x,
+                        const float *router_w, const float *bias, const uint8_t *gate, const uint8_t *up,
+                        const uint8_t *down, const int32_t *sel, int32_t n_sel, const int32_t *idx_in, double *out,
+                        int32_t *idx_out, double *w_out, double *logits_out, int q8) {
     if (H <= 0 || E <= 0 || k <= 0 || k > E || I <= 0 || T <= 0 || H % 256 || I % 256) return -1;
     int64_t nsel = sel ? n_sel : T;
     double *logits = (double *)malloc(sizeof(double) * (size_t)T * E);
@@ -328,8 +393,17 @@ int mo_forward(int32_t H, int32_t E, int32_t k, int32_t I, int32_t T, const floa
             for (int32_t j = 0; j < k; ++j) {
                 if (idx[(int64_t)t * k + j] != e) continue;
                 double *xd = (double *)malloc(sizeof(double) * (size_t)H);
-                for (int32_t c = 0; c < H; ++c) xd[c] = (double)x[(int64_t)t * H + c];
-                mo_expert_dense(H, I, Wg, Wu, Wd, xd, Y + (s * k + j) * H, NULL, NULL, NULL);
+                int bad = !xd;
+                if (!bad && q8) {
+                    bad = q8k_round_trip(H, x + (int64_t)t * H, xd) != 0;
+                } else if (!bad) {
+                    for (int32_t c = 0; c < H; ++c) xd[c] = (double)x[(int64_t)t * H + c];
+                }
+                if (!bad) bad = expert_dense_impl(H, I, Wg, Wu, Wd, xd, Y + (s * k + j) * H, NULL, NULL, NULL, q8);
+                if (bad) {
+#pragma omp atomic write
+                    rc = -1;
+                }
                 free(xd);
             }
         }
@@ -408,4 +482,24 @@ void mo_stage_stats(int64_t n, const double *v, double s[7]) {
     s[4] = mx;
     s[5] = fin ? sum / (double)fin : 0.0;
     s[6] = fin ? sqrt(sq / (double)fin) : 0.0;
+}
+
+/* The layer (described above). */
+int mo_forward(int32_t H, int32_t E, int32_t k, int32_t I, int32_t T, const float *x, const float *router_w,
+               const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
+               const int32_t *sel, int32_t n_sel, const int32_t *idx_in, double *out, int32_t *idx_out,
+               double *w_out, double *logits_out) {
+    return forward_impl(H, E, k, I, T, x, router_w, bias, gate, up, down, sel, n_sel, idx_in, out, idx_out, w_out,
+                        logits_out, 0);
+}
+
+/* The layer (arguments as mo_forward) with the routed experts' matvecs fed
+ * Q8_K-quantised activations: each token's x row, and each expert's h, enter
+ * as their mo_q8k_quantize values; the router runs on the fp32 x. */
+int mo_forward_q8(int32_t H, int32_t E, int32_t k, int32_t I, int32_t T, const float *x, const float *router_w,
+                  const float *bias, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
+                  const int32_t *sel, int32_t n_sel, const int32_t *idx_in, double *out, int32_t *idx_out,
+                  double *w_out, double *logits_out) {
+    return forward_impl(H, E, k, I, T, x, router_w, bias, gate, up, down, sel, n_sel, idx_in, out, idx_out, w_out,
+                        logits_out, 1);
 }
