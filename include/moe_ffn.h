@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-/* 2: adds moe_ffn_set_norm, moe_ffn_forward_block and moe_ffn_debug_stats. */
+/* 2: adds moe_ffn_set_norm, moe_ffn_forward_block, moe_ffn_debug_stats and moe_ffn_forward_q8. */
 #define MOE_FFN_ABI_VERSION 2
 
 typedef struct moe_ffn_s *moe_ffn_t;
@@ -116,6 +116,19 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
  * overlapping x, bad handle), OOM, DEVICE. */
 moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                            int32_t *router_idx, void *stream);
+
+/* The layer with Q8_K-style int8 activations for the routed experts (the
+ * int8-activation CPU path that qwen3_moe_dispatch.rs compares the GPU path
+ * against, trading accuracy for speed): each token's x row and each expert's h
+ * enter the expert matvecs as codes q and a scale d per 256 values, amax =
+ * max |v|, q = rint(v * (127 / amax)) in [-127, 127], d = amax / 127, all in
+ * fp32; the router runs on the fp32 x. Arguments, outputs and errors as
+ * moe_ffn_forward; this variant covers the decode path only (T <= 4 and the
+ * shapes that path takes: hidden_dim <= 4096, num_experts <= 128,
+ * num_experts_per_tok * moe_intermediate / 256 <= 48), else INVALID_SHAPE.
+ * Non-finite inputs give unspecified outputs. */
+moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                              int32_t *router_idx, void *stream);
 
 /* Set the pre-FFN norm of the block around the layer: the RMSNorm weight and
  * eps that moe_ffn_forward_block applies (forward_qwen3_moe.rs, prefill step

@@ -38,6 +38,8 @@ _lib.moe_ffn_reserve.argtypes = [_vp, ctypes.c_int32, _vp]
 _lib.moe_ffn_reserve.restype = ctypes.c_int
 _lib.moe_ffn_forward.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_forward.restype = ctypes.c_int
+_lib.moe_ffn_forward_q8.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_forward_q8.restype = ctypes.c_int
 _lib.moe_ffn_set_norm.argtypes = [_vp, _vp, ctypes.c_float, _vp]
 _lib.moe_ffn_set_norm.restype = ctypes.c_int
 _lib.moe_ffn_forward_block.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
@@ -138,6 +140,22 @@ def moe_ffn_forward(handle: int, x: torch.Tensor, out: torch.Tensor, router_out:
     st = _lib.moe_ffn_forward(_vp(handle), int(x.shape[0]), _ptr(x), _ptr(out), _ptr(router_out), _ptr(router_idx),
                               _stream(stream))
     _check(st, "moe_ffn_forward")
+
+
+def moe_ffn_forward_q8(handle: int, x: torch.Tensor, out: torch.Tensor, router_out: torch.Tensor | None = None,
+                       router_idx: torch.Tensor | None = None, stream=None) -> None:
+    """out[T][H] <- MoE FFN of x with Q8_K-style int8 expert activations (decode path: T <= 4)."""
+    _dev(x, "x", torch.float32)
+    _dev(out, "out", torch.float32)
+    if x.dim() != 2 or out.shape != x.shape:
+        raise ValueError("x and out must both be [T, hidden_dim]")
+    if router_out is not None:
+        _dev(router_out, "router_out", torch.float32)
+    if router_idx is not None:
+        _dev(router_idx, "router_idx", torch.int32)
+    st = _lib.moe_ffn_forward_q8(_vp(handle), int(x.shape[0]), _ptr(x), _ptr(out), _ptr(router_out),
+                                 _ptr(router_idx), _stream(stream))
+    _check(st, "moe_ffn_forward_q8")
 
 
 def moe_ffn_set_norm(handle: int, norm_w: torch.Tensor, eps: float, stream=None) -> None:
@@ -244,6 +262,12 @@ class MoeFfn:
         if out is None:
             out = torch.empty_like(x)
         moe_ffn_forward(self.handle, x, out, router_out, router_idx, stream)
+        return out
+
+    def forward_q8(self, x, out=None, router_out=None, router_idx=None, stream=None):
+        if out is None:
+            out = torch.empty_like(x)
+        moe_ffn_forward_q8(self.handle, x, out, router_out, router_idx, stream)
         return out
 
     def set_norm(self, norm_w, eps: float, stream=None) -> None:

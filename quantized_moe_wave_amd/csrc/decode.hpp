@@ -61,7 +61,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                                                   const float *__restrict__ bias, int T, int H, int E,
                                                   double *__restrict__ logits, f16 *__restrict__ x_hilo,
                                                   f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
-                                                  const float *__restrict__ norm_w, double eps) {
+                                                  const float *__restrict__ norm_w, double eps, int q8) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nsb = H / kQ4Weights;
     const int wpb = blockDim.x >> 6;  // waves per workgroup
@@ -72,7 +72,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
         const int t = u / nsb, b = u % nsb;
         const double ir = norm_w ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
         stage_row_sb(x + (size_t)t * H, nsb, b, x_hilo + (size_t)t * 2 * H, x_xs + (size_t)t * nsb * 16,
-                     x_sinv + (size_t)t * nsb, -10000, norm_w, ir);
+                     x_sinv + (size_t)t * nsb, -10000, norm_w, ir, q8 != 0);
     }
 
     // Loads are unconditional (chunk and token indices clamped) so that all of
@@ -290,8 +290,8 @@ __global__ __launch_bounds__(64) void router_small_kernel(const float *__restric
                                                            const float *__restrict__ bias, int T, int H, int E,
                                                            double *__restrict__ logits, f16 *__restrict__ x_hilo,
                                                            f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
-                                                           const float *__restrict__ norm_w, double eps) {
-    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv, norm_w, eps);
+                                                           const float *__restrict__ norm_w, double eps, int q8) {
+    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv, norm_w, eps, q8);
 }
 
 constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS
@@ -453,7 +453,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     const float *__restrict__ h, int I, const int32_t *__restrict__ dsel, const float *__restrict__ dw,
     const float *__restrict__ resid, float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ entries, int32_t *__restrict__ pos) {
+    int32_t *__restrict__ entries, int32_t *__restrict__ pos, int q8) {
     const int rg = blockIdx.x, t = blockIdx.y;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -516,6 +516,12 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
             int se = 10 - ex;
             se = se > 100 ? 100 : (se < -100 ? -100 : se);
             if (!(m > 0.f) || !(m < INFINITY)) se = 0;
+            if (q8) {  // Q8_K codes of this 256-value block of h (q8_code), staged with scale 1
+                const float is = m > 0.f ? 127.f / m : 0.f;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v[c] = q8_code(v[c], is);
+                se = 0;
+            }
             const float scl = ldexpf(1.f, se);
             const int s = lane >> 3, gg = (lane & 7) >> 1, half = lane & 1;
             float part_sum = 0.f;
@@ -537,7 +543,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
                 axs[wave][s] = hs;
                 axs[wave][8 + s] = (f16)(part_sum - (float)hs);
             }
-            if (lane == 0) asinv[wave] = ldexpf(1.f, -se);
+            if (lane == 0) asinv[wave] = q8 ? m / 127.f : ldexpf(1.f, -se);
             lds_wave_sync();
 
             const bool a_ok = (n == 0);

@@ -336,8 +336,10 @@ bool decode_path(const moe_ffn_shape &s, int T) {
 // to the output by the kernel that writes it (the block's residual add).
 // norm_w (decode path only): x is the residual stream and the router launch
 // applies the block's RMSNorm (weight norm_w, eps) to every value it reads.
+// q8 (decode path only): the experts' matvecs take Q8_K-style codes of x and h
+// (stage_row_sb and down_combine_small_kernel stage the codes instead).
 moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out, int32_t *router_idx,
-                         const float *resid, const float *norm_w, double eps, hipStream_t st) {
+                         const float *resid, const float *norm_w, double eps, int q8, hipStream_t st) {
     const moe_ffn_shape &s = h->sh;
     const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
     moe_status r = ensure_ws(h, T, st);
@@ -349,16 +351,17 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
     Profiler &pf = h->prof;
-    if (norm_w && !decode_path(s, T)) return fail(MOE_ERR_INVALID_ARG, "internal: fused norm off the decode path");
+    if ((norm_w || q8) && !decode_path(s, T))
+        return fail(MOE_ERR_INVALID_ARG, "internal: fused norm or Q8_K staging off the decode path");
     if (decode_path(s, T)) {
         // decode path: three launches (see decode.hpp)
         launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
-               w.logits, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps);
+               w.logits, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, q8);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
         launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
                H / kRowGroup, ni, w.logits, E, T, k, w.h, I, w.dsel, w.dw, resid, out, H, idx, wt, w.counts, w.offsets,
-               w.entries, w.pos);
+               w.entries, w.pos, q8);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
         h->last_T = T;
@@ -559,7 +562,20 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     g_err.clear();
     moe_status r = check_call(h, T, x, out, router_out, router_idx);
     if (r != MOE_OK) return r;
-    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, (hipStream_t)stream);
+    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 0, (hipStream_t)stream);
+}
+
+moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                              int32_t *router_idx, void *stream) {
+    g_err.clear();
+    moe_status r = check_call(h, T, x, out, router_out, router_idx);
+    if (r != MOE_OK) return r;
+    if (!decode_path(h->sh, T))
+        return fail(MOE_ERR_INVALID_SHAPE,
+                    "the Q8_K-activation variant covers the decode path only (at most %d tokens, hidden_dim <= %d, "
+                    "num_experts <= %d, num_experts_per_tok * moe_intermediate / 256 <= %d); got T = %d",
+                    kSmallT, kSmallMaxH, kRankMaxExperts, kMaxTopK * 6, T);
+    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 1, (hipStream_t)stream);
 }
 
 moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *stream) {
@@ -592,12 +608,13 @@ moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, fl
     hipStream_t st = (hipStream_t)stream;
     // decode path: the norm is fused into its router launch
     if (decode_path(h->sh, T))
-        return forward_layer(h, T, hidden, out, router_out, router_idx, hidden, h->norm_w, (double)h->norm_eps, st);
+        return forward_layer(h, T, hidden, out, router_out, router_idx, hidden, h->norm_w, (double)h->norm_eps, 0,
+                             st);
     r = ensure_ws(h, T, st);
     if (r != MOE_OK) return r;
     launch(h->prof, kStNorm, rmsnorm_kernel, dim3(T), dim3(256), st, hidden, h->norm_w, h->sh.hidden_dim,
            (double)h->norm_eps, h->ws.xn);
-    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, nullptr, 0.0, st);
+    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, nullptr, 0.0, 0, st);
 }
 
 moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets, int32_t *entries,

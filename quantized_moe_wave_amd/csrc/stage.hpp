@@ -31,10 +31,16 @@ __device__ __forceinline__ int stage_exponent(float m) {
 // columns); lanes 0..31 each own one 8-column fragment.
 // With nw (the block's RMSNorm weight, or null) the staged values are the
 // normalised row: fp32(src[c] * nw[c] * inv_rms), the product in double.
+// q8: Q8_K-style codes instead (q8_code: per super-block, amax = max |v|,
+// q = rint(v * (127 / amax)) in [-127, 127], all in fp32); hi holds q (exact
+// in fp16), lo 0, the sums are sums of q (exact), and 1/s is d = amax / 127.
+__device__ __forceinline__ float q8_code(float v, float iscale) {
+    return fminf(fmaxf(rintf(v * iscale), -127.f), 127.f);
+}
 __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int nsb, int b, f16 *__restrict__ hilo_row,
                                              f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
                                              int se = -10000, const float *__restrict__ nw = nullptr,
-                                             double inv_rms = 1.0) {
+                                             double inv_rms = 1.0, bool q8 = false) {
     const int lane = threadIdx.x & 63;
     const int f = lane & 31;  // fragment: k-step s = f / 4, lane group g = f % 4
     const int s = f >> 2, g = f & 3;
@@ -54,7 +60,18 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = (float)((double)v[i] * w[i] * inv_rms);
     }
-    if (se < -1000) {
+    float q8_d = 0.f;
+    if (q8) {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+        m = wave_max(lane < 32 ? m : 0.f);
+        const float is = m > 0.f ? 127.f / m : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = q8_code(v[i], is);  // codes, staged with scale 1 below
+        q8_d = m / 127.f;
+        se = 0;
+    } else if (se < -1000) {
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -86,7 +103,7 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
             xd[s] = h;
             xd[8 + s] = (f16)(part - (float)h);
         }
-        if (lane == 0) sinv_row[b] = ldexpf(1.f, -se);
+        if (lane == 0) sinv_row[b] = q8 ? q8_d : ldexpf(1.f, -se);
     }
 }
 

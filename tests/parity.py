@@ -64,8 +64,9 @@ def make_layer(inp: synth.LayerInputs, dev_inputs=None):
     return layer, d
 
 
-def run_gpu(layer, x_dev, block: bool = False) -> GpuRun:
-    """One forward (block: forward_block, x_dev then being the residual stream) and its routing state."""
+def run_gpu(layer, x_dev, block: bool = False, q8: bool = False) -> GpuRun:
+    """One forward (block: forward_block, x_dev then being the residual stream; q8: forward_q8) and its routing
+    state."""
     import torch
 
     import quantized_moe_wave_amd as q
@@ -77,6 +78,8 @@ def run_gpu(layer, x_dev, block: bool = False) -> GpuRun:
     idx = torch.empty((T, k), dtype=torch.int32, device=x_dev.device)
     if block:
         layer.forward_block(x_dev, out, w, idx)
+    elif q8:
+        layer.forward_q8(x_dev, out, w, idx)
     else:
         layer.forward(x_dev, out, w, idx)
     logits = torch.empty((T, E), dtype=torch.float64, device=x_dev.device)
@@ -106,11 +109,11 @@ def out_errors(gpu: np.ndarray, ref: np.ndarray):
     return float(max_rel), float(l1_rel)
 
 
-def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None, resid=None):
+def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None, resid=None, q8: bool = False):
     """Assert the bar. sel: token subset for the expert part (None = all). resid: the block's residual stream
     [T][H] (inp.x then holds the normalised rows the layer ran on); the reference output is resid + layer."""
     k, E = inp.wl.top_k, inp.wl.experts
-    ref = oracle.forward(inp.x, inp.router, inp.bias, inp.gate, inp.up, inp.down, k, sel=sel)
+    ref = oracle.forward(inp.x, inp.router, inp.bias, inp.gate, inp.up, inp.down, k, sel=sel, q8=q8)
     T = inp.x.shape[0]
     tokens = np.arange(T) if sel is None else np.asarray(sel)
 
@@ -146,7 +149,7 @@ def check_parity(inp: synth.LayerInputs, g: GpuRun, sel=None, report=None, resid
     td = tie_diff[tokens]
     if td.any():
         forced = oracle.forward(inp.x, inp.router, inp.bias, inp.gate, inp.up, inp.down, k, sel=tokens[td],
-                                idx_in=g.idx)
+                                idx_in=g.idx, q8=q8)
         ref_out[td] = forced["out"]
     if resid is not None:
         ref_out = oracle.add_residual(np.ascontiguousarray(resid[tokens]), ref_out)
