@@ -24,6 +24,9 @@ The layer inside its block (moe_ffn_forward_block: pre-FFN RMSNorm, the layer, r
 add) is timed the same way on the decode and prefill workloads under "block", with the
 time of one per-stage statistics call (moe_ffn_debug_stats) on the last token.
 
+The decode layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8) is timed
+the same way under "q8_activations".
+
 The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
 For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
 (the decode kernels' weight bytes) the same way.
@@ -81,7 +84,7 @@ def parse_args():
 class Bench:
     """R replicas of one workload on the GPU, with their outputs preallocated."""
 
-    def __init__(self, wl, replicas: int, seed: int = 1, block: bool = False):
+    def __init__(self, wl, replicas: int, seed: int = 1, block: bool = False, q8: bool = False):
         import torch
 
         import synth
@@ -89,6 +92,7 @@ class Bench:
 
         self.wl = wl
         self.block = block
+        self.q8 = q8
         self.layers, self.xs, self.outs, self.ws, self.idxs = [], [], [], [], []
         self.host0 = None
         for r in range(replicas):
@@ -119,6 +123,8 @@ class Bench:
         r = i % self.R
         if self.block:
             self.layers[r].forward_block(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+        elif self.q8:
+            self.layers[r].forward_q8(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
         else:
             self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
 
@@ -395,6 +401,23 @@ def measure_block(wl, steps: int, eager: bool) -> dict:
             "stage_stats_us": round(stats_us, 2)}
 
 
+def measure_q8(wl, steps: int, eager: bool) -> dict:
+    """The layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8, decode path), timed like the main
+    step."""
+    import torch
+
+    b = Bench(wl, replicas_for(wl), q8=True)
+    try:
+        ms = b.timed(steps, max(3, steps // 10), eager)
+    finally:
+        b.close()
+        del b
+        torch.cuda.empty_cache()
+    log(f"{wl.name} q8 activations: {ms * 1e3:.2f} us/step")
+    return {"workload": wl.name, "tokens": wl.tokens, "steps": steps, "ms_per_step": round(ms, 5),
+            "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1)}
+
+
 def cpu_baseline(inp, seconds: float):
     """The oracle on T=1 forwards of replica 0's weights, one token per call, for ~seconds."""
     import numpy as np
@@ -530,6 +553,8 @@ def main() -> int:
         line["block"] = [measure_block(wl, args.steps, args.eager)]
         if not args.no_prefill:
             line["block"].append(measure_block(synth.WORKLOADS[args.prefill_workload], args.prefill_steps, args.eager))
+    if wl.tokens <= 4:
+        line["q8_activations"] = measure_q8(wl, args.steps, args.eager)
     line["hbm_step"]["plain_copy_probe"] = copy_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]
     if extras:
