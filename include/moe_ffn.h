@@ -118,8 +118,9 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
                            int32_t *router_idx, void *stream);
 
 /* The layer with Q8_K-style int8 activations for the routed experts (the
- * int8-activation CPU path that qwen3_moe_dispatch.rs compares the GPU path
- * against, trading accuracy for speed): each token's x row and each expert's h
+ * activation format of the production CPU path in qwen3_moe_dispatch.rs, doc
+ * of cpu_reference, whose logits differ measurably from the fp32-activation
+ * forward's): each token's x row and each expert's h
  * enter the expert matvecs as codes q and a scale d per 256 values, amax =
  * max |v|, q = rint(v * (127 / amax)) in [-127, 127], d = amax / 127, all in
  * fp32; the router runs on the fp32 x. Arguments, outputs and errors as
