@@ -66,3 +66,36 @@ def test_block_needs_a_norm_weight():
     with pytest.raises(q.MoeError):
         layer.set_norm(torch.ones(inp.wl.hidden), float("nan"))
     layer.close()
+
+
+@pytest.mark.parametrize("name,T,mode", [("30b-batch", 64, "block"), ("30b-decode", 2, "block"),
+                                         ("30b-decode", 2, "q8")])
+def test_graph_replay_matches_eager(name, T, mode):
+    """The block (norm launch or fused norm) and the int8-activation variant captured in a HIP graph, replayed
+    several times with eager work and synchronisations between replays: every replay equals the eager call,
+    bit for bit."""
+    import torch
+
+    print(f"[block] graph replay {name} T={T} {mode}", flush=True)
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl, seed=13, tokens=T)
+    layer, dev = parity.make_layer(inp)
+    layer.set_norm(torch.from_numpy(synth.gen_norm(13, 0, wl.hidden)), synth.NORM_EPS)
+    layer.reserve(T)
+    x = dev["x"]
+    run = layer.forward_block if mode == "block" else layer.forward_q8
+    eager = run(x).cpu().numpy()
+    out = torch.empty_like(x)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, capture_error_mode="relaxed"):
+        run(x, out)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        layer.forward(x[:1], torch.empty_like(x[:1]))  # eager work on the same handle between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), rep
+    del g
+    layer.close()
