@@ -9,12 +9,15 @@ measured beside it and reported under "prefill".
 
 Timing: W warmup steps, then K steps captured in one HIP graph and replayed
 between two events on the launch stream, with device synchronisation on both
-sides. Steps cycle over R replicas of the layer (distinct weights and inputs)
-whose weights total >= 1 GB, so the 256 MB Infinity Cache cannot hold the
-working set. The dominant kernel (gate_up) is then timed over K more eager
-steps with events stamped at its own start and end (hipExtLaunchKernelGGL);
-its roofline fraction uses algorithmic bytes (decode: routed gate+up Q4_K
-weight bytes) or flops (prefill: 2*T*k*2*H*I) per launch.
+sides. Steps cycle over R replicas of the layer (distinct weights) whose
+weights total >= 1 GB, and for T <= 64 over a pool of P = 64 distinct input
+batches per replica, so consecutive steps route to different experts: over
+the timed loop the experts touched total far more than the 256 MB Infinity
+Cache (the JSON line states the union). The dominant kernel is then timed
+over K more eager steps with events stamped at its own start and end
+(hipExtLaunchKernelGGL); its roofline fraction uses algorithmic bytes (the
+routed gate+up Q4_K weight bytes of its launch) or flops (2 * rows * 2I * H
+for the 64-row grouped GEMM) per launch.
 
 Single eager steps (median, 10th / 90th percentile) go under "step_us": "warm" with
 only a GPU sleep between steps, "cold" with a 512 MB write between steps (outside
@@ -27,9 +30,11 @@ time of one per-stage statistics call (moe_ffn_debug_stats) on the last token.
 The decode layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8) is timed
 the same way under "q8_activations".
 
-The 64-token batch and the 235b-shaped layer are timed as whole steps under "others".
-For context, hbm_step.plain_copy_probe times a plain device copy of 7, 14 and 21 MiB
-(the decode kernels' weight bytes) the same way.
+The 64-token batch and the 235b-shaped layer are timed as whole steps, each with
+the roofline of its own dominant kernels, under "others". For context,
+hbm_step.plain_read_probe times a plain read-only device reduction (torch) of 7,
+14 and 21 MiB (the decode kernels' weight bytes) the same way: one HIP graph
+cycling over >= 1 GB of sources, so each read comes from HBM.
 
 The CPU baseline is the fp64 oracle as it stands, timed on this host on a
 bounded sample of the same workload.
@@ -53,6 +58,10 @@ METRIC = "MoE-FFN tokens/s per layer + HBM GB/s (decode), MFMA TFLOP/s (prefill)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
 REPLICA_BYTES = 1 << 30        # weights cycled per timed loop
+X_POOL = 64                    # distinct input batches per replica for T <= POOL_MAX_T
+POOL_MAX_T = 64
+SMALL_BUCKET = 16              # buckets of at most this many pairs take the 16-row GEMM
+DTYPE = "q4k x fp32 (fp16 hi+lo MFMA, fp32 acc; fp64 router)"
 
 
 def log(msg: str) -> None:
@@ -69,8 +78,12 @@ def parse_args():
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-block", action="store_true", help="skip timing the layer inside its block")
+    ap.add_argument("--no-q8", action="store_true", help="skip timing the int8-activation variant")
+    ap.add_argument("--no-probe", action="store_true", help="skip the plain read probe")
+    ap.add_argument("--no-steps-dist", action="store_true", help="skip the single-step warm/cold distribution")
     ap.add_argument("--extra-workloads", default="30b-batch,235b-shape",
-                    help="comma-separated workloads whose whole-step time is reported under \"others\" ('' for none)")
+                    help="comma-separated workloads whose step time and kernel rooflines go under \"others\" "
+                         "('' for none)")
     ap.add_argument("--extra-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -81,35 +94,46 @@ def parse_args():
     return ap.parse_args()
 
 
+def upload_layer(inp):
+    """The layer of one replica's host inputs, and its input batch on the device."""
+    import torch
+
+    import quantized_moe_wave_amd as q
+
+    wl = inp.wl
+    layer = q.MoeFfn.from_host(wl.hidden, wl.experts, wl.top_k, wl.inter, inp.gate, inp.up, inp.down, inp.router,
+                               inp.bias)
+    return layer, torch.from_numpy(inp.x).cuda()
+
+
 class Bench:
-    """R replicas of one workload on the GPU, with their outputs preallocated."""
+    """R replicas of one workload on the GPU (each with a pool of P input batches), outputs preallocated."""
 
     def __init__(self, wl, replicas: int, seed: int = 1, block: bool = False, q8: bool = False):
         import torch
 
         import synth
-        from tests import parity
 
         self.wl = wl
         self.block = block
         self.q8 = q8
+        self.P = X_POOL if wl.tokens <= POOL_MAX_T else 1
         self.layers, self.xs, self.outs, self.ws, self.idxs = [], [], [], [], []
         self.host0 = None
         for r in range(replicas):
             log(f"{wl.name}: generating replica {r + 1}/{replicas}")
             inp = synth.make_inputs(wl, seed=seed, replica=r)
-            dev = parity.upload(inp)
-            layer, _ = parity.make_layer(inp, dev)
+            layer, x = upload_layer(inp)
             layer.reserve(wl.tokens)
             if block:
                 layer.set_norm(torch.from_numpy(synth.gen_norm(seed, r, wl.hidden)), synth.NORM_EPS)
-            x = dev["x"]
-            for key in ("gate", "up", "down", "router", "bias"):
-                dev[key] = None  # the layer owns its copies
+            # pool entry 0 is the replica's own x; the others are further seeded draws of the same distribution
+            pool = [x] + [torch.from_numpy(synth.gen_x(seed + 1000 + p, r, wl.tokens, wl.hidden)).cuda()
+                          for p in range(1, self.P)]
             if r == 0:
                 self.host0 = inp
             self.layers.append(layer)
-            self.xs.append(x)
+            self.xs.append(pool)
             self.outs.append(torch.empty_like(x))
             self.ws.append(torch.empty((wl.tokens, wl.top_k), dtype=torch.float32, device=x.device))
             self.idxs.append(torch.empty((wl.tokens, wl.top_k), dtype=torch.int32, device=x.device))
@@ -119,30 +143,51 @@ class Bench:
     def R(self):
         return len(self.layers)
 
+    def slot(self, i: int):
+        """(replica, pool entry) of step i."""
+        return i % self.R, (i // self.R) % self.P
+
     def step(self, i: int) -> None:
-        r = i % self.R
+        r, p = self.slot(i)
+        x = self.xs[r][p]
         if self.block:
-            self.layers[r].forward_block(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+            self.layers[r].forward_block(x, self.outs[r], self.ws[r], self.idxs[r])
         elif self.q8:
-            self.layers[r].forward_q8(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+            self.layers[r].forward_q8(x, self.outs[r], self.ws[r], self.idxs[r])
         else:
-            self.layers[r].forward(self.xs[r], self.outs[r], self.ws[r], self.idxs[r])
+            self.layers[r].forward(x, self.outs[r], self.ws[r], self.idxs[r])
 
     def routing(self):
-        """Per replica: (distinct experts U, max tokens on one expert, rows in GEMM buckets)."""
+        """Per (replica, pool entry): its expert counts (from the layer's own routing)."""
         import numpy as np
         import torch
 
+        self.counts = {}
         for r in range(self.R):
-            self.step(r)
-        torch.cuda.synchronize()
-        stats = []
-        for r in range(self.R):
-            idx = self.idxs[r].cpu().numpy()
-            cnt = np.bincount(idx.ravel(), minlength=self.wl.experts)
-            # rows that take the grouped GEMM: buckets of more than 16 entries
-            stats.append((int((cnt > 0).sum()), int(cnt.max()), int(cnt[cnt > 16].sum())))
-        return stats
+            for p in range(self.P):
+                self.step(r + self.R * p)
+                torch.cuda.synchronize()
+                idx = self.idxs[r].cpu().numpy()
+                self.counts[(r, p)] = np.bincount(idx.ravel(), minlength=self.wl.experts)
+        return self.counts
+
+    def step_stats(self, i: int) -> dict:
+        """Routing figures of step i: distinct experts U, largest bucket, pairs in 64-row GEMM buckets, experts
+        in 16-row buckets."""
+        c = self.counts[self.slot(i)]
+        return {"U": int((c > 0).sum()), "max": int(c.max()), "rows_big": int(c[c > SMALL_BUCKET].sum()),
+                "small": int(((c > 0) & (c <= SMALL_BUCKET)).sum())}
+
+    def touched(self, steps: int) -> dict:
+        """Union of experts touched per replica over steps 0..steps-1, and their weight bytes."""
+        import numpy as np
+
+        seen = [np.zeros(self.wl.experts, bool) for _ in range(self.R)]
+        for i in range(steps):
+            r, p = self.slot(i)
+            seen[r] |= self.counts[(r, p)] > 0
+        per = [int(s.sum()) for s in seen]
+        return {"experts_per_replica": per, "bytes": int(sum(per) * self.wl.expert_bytes)}
 
     def timed(self, steps: int, warmup: int, eager: bool) -> float:
         """Milliseconds per step."""
@@ -211,7 +256,7 @@ class Bench:
         return res
 
     def stage_times(self, steps: int, stages) -> dict:
-        """{stage: [(replica, total ms, launches)]} from kernel-stamped events over `steps` eager steps."""
+        """{stage: (total ms, launches)} from kernel-stamped events over eager steps 0..steps-1."""
         import torch
 
         import quantized_moe_wave_amd as q
@@ -221,12 +266,13 @@ class Bench:
         for i in range(steps):
             self.step(i)
         torch.cuda.synchronize()
-        res = {s: [] for s in stages}
-        for r, layer in enumerate(self.layers):
+        res = {s: [0.0, 0] for s in stages}
+        for layer in self.layers:
             got = q.moe_ffn_profile_read(layer.handle)
             q.moe_ffn_profile(layer.handle, [])
             for s in stages:
-                res[s].append((r, got[s][0], got[s][1]))
+                res[s][0] += got[s][0]
+                res[s][1] += got[s][1]
         return res
 
     def close(self):
@@ -235,14 +281,14 @@ class Bench:
         self.layers = []
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per dispatch of `kernel` from profiles/hbm_traffic.md (rocprofv3 FETCH_SIZE / WRITE_SIZE,
-    scaled by the plain-copy calibration), or None if not measured or if the kernel's sources changed since."""
+def profile_record(kernel: str, which: str):
+    """Per-dispatch counter figures of `kernel` committed under profiles/ (which = "traffic": HBM bytes from
+    rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by the plain-copy calibration; "sq": MFMA-busy and VALU figures from SQ
+    counters), or None if not measured or if the kernel's sources changed since (hash of the listed files)."""
     import hashlib
     import re
 
-    here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md" if which == "traffic" else "sq_counters.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
@@ -254,10 +300,12 @@ def measured_traffic(kernel: str):
         return None
     h = hashlib.sha256()
     for f in k["files"]:
-        h.update(open(os.path.join(here, "quantized_moe_wave_amd", "csrc", f), "rb").read())
+        h.update(open(os.path.join(ROOT, "quantized_moe_wave_amd", "csrc", f), "rb").read())
     if h.hexdigest()[:16] != k["source_hash"]:
         return None
-    return int(round((k["fetch_kib"] * data["fetch_factor"] + k["write_kib"] * data["write_factor"]) * 1024))
+    if which == "traffic":
+        return int(round((k["fetch_kib"] * data["fetch_factor"] + k["write_kib"] * data["write_factor"]) * 1024))
+    return {key: k[key] for key in ("mfma_busy", "valu_per_mfma") if key in k}
 
 
 def replicas_for(wl) -> int:
@@ -269,102 +317,118 @@ def gate_up_bytes_per_expert(wl) -> int:
     return 2 * wl.hidden * wl.inter * 144 // 256
 
 
-def measure(wl, steps: int, warmup: int, eager: bool, bound: str, want_stages: bool):
-    b = Bench(wl, replicas_for(wl))
-    try:
-        stats = b.routing()
-        log(f"{wl.name}: routing per replica (distinct experts, max tokens/expert) = {stats}")
-        ms = b.timed(steps, warmup, eager)
-        log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'})")
-        T, k, H, I = wl.tokens, wl.top_k, wl.hidden, wl.inter
-        if bound == "hbm":
-            # decode: the gate/up kernel; routed gate+up weight bytes of each launch
-            # (T <= 4: the per-pair decode kernel, else the 16-row grouped GEMM)
-            stage = "gate_up"
-            kname = "gateup_pair_kernel" if T <= 4 else "expert_gemm_kernel<gate_up, 16-row tiles>"
-            prof = b.stage_times(steps, [stage])[stage]
-            total_ms = sum(p[1] for p in prof)
-            launches = sum(p[2] for p in prof)
-            if launches == 0 or total_ms <= 0:
-                raise RuntimeError(f"{wl.name}: no {stage} launches were timed")
-            alg = sum(stats[r][0] * gate_up_bytes_per_expert(wl) * nl for r, _, nl in prof)
-            achieved = alg / (total_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(kname) if T <= 4 else None,
-                    "kernel": f"{kname} ({stage})", "avg_us": round(total_ms / launches * 1e3, 3),
-                    "algorithmic_bytes_per_launch": int(round(alg / launches))}
-        else:
-            # prefill: the gate/up grouped GEMM (its 8-wave launch plus the 4-wave launch that runs the split
-            # last-round tiles, when there is one); 2 * rows * 2I * H flops per step
-            import quantized_moe_wave_amd as q
-
-            stage = "gate_up_big"
-            tail = "gate_up_tail" if "gate_up_tail" in q.moe_ffn_stage_names() else None
-            both = b.stage_times(steps, [stage] + ([tail] if tail else []))
-            prof = [(r, ms + (both[tail][i][1] if tail else 0.0), nl) for i, (r, ms, nl) in enumerate(both[stage])]
-            total_ms = sum(p[1] for p in prof)
-            launches = sum(p[2] for p in prof)
-            if launches == 0 or total_ms <= 0:
-                raise RuntimeError(f"{wl.name}: no {stage} launches were timed")
-            flops = sum(2.0 * stats[r][2] * 2 * I * H * nl for r, _, nl in prof)
-            achieved = flops / (total_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": measured_traffic("expert_gemm_kernel<gate_up, 64-row tiles>"),
-                    "kernel": "expert_gemm_kernel<gate_up, 64-row tiles> (gate_up_big + gate_up_tail)",
-                    "avg_us": round(total_ms / launches * 1e3, 3)}
-        avg_us = total_ms / launches * 1e3
-        log(f"{wl.name}: {stage} avg {avg_us:.2f} us/launch -> {roof['achieved']} {roof['unit']}")
-        if want_stages:
-            import quantized_moe_wave_amd as q
-
-            allp = b.stage_times(steps, q.moe_ffn_stage_names())
-            for s, lst in allp.items():
-                tm = sum(p[1] for p in lst)
-                n = sum(p[2] for p in lst)
-                log(f"{wl.name}: stage {s:8s} {tm / max(n, 1) * 1e3:9.2f} us avg over {n} launches")
-        U = sum(st[0] for st in stats) / len(stats)
-        roof_steps = b.per_step(max(20, min(steps, 200)))
-        return b, ms, stats, roof, U, roof_steps
-    except Exception:
-        b.close()
-        raise
+# The kernels a roofline can be reported for: (stage names summed per step, bound, profile key)
+KERNELS = {
+    "decode": (["gate_up"], "hbm", "gateup_pair_kernel"),
+    "small": (["gate_up"], "hbm", "expert_gemm_kernel<gate_up, 16-row tiles>"),
+    "big": (["gate_up_big", "gate_up_tail"], "mfma", "expert_gemm_kernel<gate_up, 64-row tiles>"),
+}
 
 
-def measure_step(wl, steps: int, eager: bool, want_stages: bool = False) -> dict:
-    """Whole-step time of one more workload: tokens/s and the step's routed-expert bytes and algorithmic flops
-    against the HBM and MFMA peaks."""
+def kernel_roofline(b: Bench, steps: int, kind: str) -> dict | None:
+    """Roofline of one gate/up kernel over `steps` eager steps: algorithmic work of every launch / its
+    kernel-stamped time. decode: the per-pair decode kernel, bytes = U * routed gate+up bytes per expert; small: the
+    16-row grouped GEMM, bytes = (experts with 1..16 pairs) * gate+up bytes per expert; big: the 64-row grouped GEMM
+    (its 8-wave launch + the launch of the last-round halves), flops = 2 * rows * 2I * H."""
+    import quantized_moe_wave_amd as q
+
+    stages, bound, pkey = KERNELS[kind]
+    stages = [s for s in stages if s in q.moe_ffn_stage_names()]
+    got = b.stage_times(steps, stages)
+    total_ms = sum(got[s][0] for s in stages)
+    launches = got[stages[0]][1]
+    if launches == 0 or total_ms <= 0:
+        return None
+    wl = b.wl
+    st = [b.step_stats(i) for i in range(steps)]
+    if bound == "hbm":
+        per = "U" if kind == "decode" else "small"
+        work = sum(s[per] for s in st) * gate_up_bytes_per_expert(wl)
+        achieved = work / (total_ms * 1e-3) / 1e9
+        rec = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profile_record(pkey, "traffic"),
+               "algorithmic_bytes_per_launch": int(round(work / launches))}
+    else:
+        work = sum(2.0 * s["rows_big"] * 2 * wl.inter * wl.hidden for s in st)
+        achieved = work / (total_ms * 1e-3) / 1e12
+        rec = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+               "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": profile_record(pkey, "traffic"),
+               "algorithmic_flops_per_launch": round(work / launches)}
+        sq = profile_record(pkey, "sq")
+        if sq:
+            rec.update(sq)
+    rec["kernel"] = f"{pkey} ({' + '.join(stages)})"
+    rec["avg_us"] = round(total_ms / launches * 1e3, 3)
+    log(f"{wl.name}: {rec['kernel']} avg {rec['avg_us']:.2f} us/launch -> {rec['achieved']} {rec['unit']} "
+        f"({rec['frac']:.3f} of peak)")
+    return rec
+
+
+def kinds_for(b: Bench):
+    """Roofline kernels of a workload, dominant first."""
+    if b.wl.tokens <= 4:
+        return ["decode"]
+    st = [b.step_stats(i) for i in range(b.R * b.P)]
+    has_big = any(s["rows_big"] for s in st)
+    has_small = any(s["small"] for s in st)
+    return (["big"] if has_big else []) + (["small"] if has_small else [])
+
+
+def log_stages(b: Bench, steps: int) -> None:
+    import quantized_moe_wave_amd as q
+
+    for s, (tm, n) in b.stage_times(steps, q.moe_ffn_stage_names()).items():
+        if n:
+            log(f"{b.wl.name}: stage {s:12s} {tm / n * 1e3:9.2f} us avg over {n} launches")
+
+
+def measure(wl, steps: int, warmup: int, eager: bool, want_stages: bool, dist: bool = True) -> dict:
+    """Step time, the roofline of the workload's kernels, the experts touched, and the single-step distribution."""
     import torch
 
     b = Bench(wl, replicas_for(wl))
     try:
-        stats = b.routing()
-        ms = b.timed(steps, max(3, steps // 10), eager)
+        b.routing()
+        ms = b.timed(steps, warmup, eager)
+        st = [b.step_stats(i) for i in range(steps)]
+        U = sum(s["U"] for s in st) / steps
+        touched = b.touched(steps)
+        log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'}); "
+            f"mean U {U:.1f}; experts touched over the loop {touched}")
+        roofs = [r for r in (kernel_roofline(b, steps, k) for k in kinds_for(b)) if r]
         if want_stages:
-            import quantized_moe_wave_amd as q
-
-            for st, lst in b.stage_times(steps, q.moe_ffn_stage_names()).items():
-                n = sum(p[2] for p in lst)
-                if n:
-                    log(f"{wl.name}: stage {st:12s} {sum(p[1] for p in lst) / n * 1e3:9.2f} us avg over {n} launches")
+            log_stages(b, steps)
+        res = {"ms": ms, "U": U, "max_tokens_per_expert": max(s["max"] for s in st),
+               "gemm_rows": sum(s["rows_big"] for s in st) / steps, "touched": touched, "roofs": roofs}
+        if dist:
+            res["dist"] = b.per_step(max(20, min(steps, 200)))
+        res["host0"] = b.host0
+        return res
     finally:
         b.close()
         del b
         torch.cuda.empty_cache()
-    log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps; routing per replica {stats}")
-    U = sum(st[0] for st in stats) / len(stats)
+
+
+def step_line(wl, m: dict) -> dict:
+    """Throughput of a measured workload: tokens/s, routed-expert bytes and algorithmic flops against the peaks."""
     T, k, H, I, E = wl.tokens, wl.top_k, wl.hidden, wl.inter, wl.experts
-    step_bytes = U * wl.expert_bytes
+    sec = m["ms"] * 1e-3
+    step_bytes = m["U"] * wl.expert_bytes
     flops = 2.0 * T * k * 3 * H * I + 2.0 * T * E * H
-    sec = ms * 1e-3
-    return {"workload": wl.name, "tokens": T, "steps": steps, "ms_per_step": round(ms, 5),
-            "tokens_per_s": round(T / sec, 1), "distinct_experts": U,
-            "max_tokens_per_expert": max(st[1] for st in stats),
-            "hbm_step": {"routed_expert_bytes": int(step_bytes), "achieved_gbs": round(step_bytes / sec / 1e9, 1),
-                         "frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4)},
-            "mfma_step": {"algorithmic_tflops": round(flops / sec / 1e12, 2),
-                          "frac": round(flops / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}}
+    out = {"workload": wl.name, "tokens": T, "ms_per_step": round(m["ms"], 5), "tokens_per_s": round(T / sec, 1),
+           "distinct_experts": m["U"], "max_tokens_per_expert": m["max_tokens_per_expert"],
+           "hbm_step": {"routed_expert_bytes": int(step_bytes), "achieved_gbs": round(step_bytes / sec / 1e9, 1),
+                        "frac": round(step_bytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                        "experts_touched": m["touched"]},
+           "mfma_step": {"algorithmic_tflops": round(flops / sec / 1e12, 2),
+                         "frac": round(flops / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+           "rooflines": m["roofs"]}
+    if "dist" in m:
+        out["step_us"] = m["dist"]
+        cold = m["dist"]["cold"]["median"] * 1e-6
+        out["hbm_step"]["cold_frac"] = round(step_bytes / cold / 1e9 / HBM_PEAK_GBS, 4)
+    return out
 
 
 def measure_block(wl, steps: int, eager: bool) -> dict:
@@ -377,9 +441,8 @@ def measure_block(wl, steps: int, eager: bool) -> dict:
     b = Bench(wl, replicas_for(wl), block=True)
     try:
         ms = b.timed(steps, max(3, steps // 10), eager)
-        st = b.stage_times(steps, ["norm"])["norm"]
-        n = sum(p[2] for p in st)
-        norm_us = sum(p[1] for p in st) / max(n, 1) * 1e3
+        tm, n = b.stage_times(steps, ["norm"])["norm"]
+        norm_us = tm / max(n, 1) * 1e3
         # the per-stage statistics of the last token after a block step (the traced path's summary)
         b.step(0)
         stats = torch.empty((4, 7), dtype=torch.float64, device="cuda")
@@ -398,12 +461,11 @@ def measure_block(wl, steps: int, eager: bool) -> dict:
     log(f"{wl.name} block: {ms * 1e3:.2f} us/step, norm kernel {norm_us:.2f} us, stage statistics {stats_us:.2f} us")
     return {"workload": wl.name, "tokens": wl.tokens, "steps": steps, "ms_per_step": round(ms, 5),
             "tokens_per_s": round(wl.tokens / (ms * 1e-3), 1), "norm_kernel_us": round(norm_us, 3),
-            "stage_stats_us": round(stats_us, 2)}
+            "norm_launches_per_step": round(n / steps, 3), "stage_stats_us": round(stats_us, 2)}
 
 
 def measure_q8(wl, steps: int, eager: bool) -> dict:
-    """The layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8, decode path), timed like the main
-    step."""
+    """The layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8), timed like the main step."""
     import torch
 
     b = Bench(wl, replicas_for(wl), q8=True)
@@ -420,8 +482,6 @@ def measure_q8(wl, steps: int, eager: bool) -> dict:
 
 def cpu_baseline(inp, seconds: float):
     """The oracle on T=1 forwards of replica 0's weights, one token per call, for ~seconds."""
-    import numpy as np
-
     import oracle
     import synth
 
@@ -439,9 +499,10 @@ def cpu_baseline(inp, seconds: float):
             "sample": f"{n} single-token forwards of the {wl.name} layer (replica 0 weights), {el:.1f} s"}
 
 
-def copy_probe(sizes_mb=(7, 14, 21), steps: int = 200) -> dict:
-    """Context for the decode roofline: a plain device copy (torch) of the decode kernels' byte counts, timed like a
-    step (one HIP graph of `steps` copies cycling over >= 1 GB of sources, so the caches are cold)."""
+def read_probe(sizes_mb=(7, 14, 21), steps: int = 200) -> dict:
+    """Context for the decode roofline: a plain read-only reduction (torch.sum) over the decode kernels' byte
+    counts, timed like a step (one HIP graph of `steps` reductions cycling over >= 1 GB of sources, so each read
+    comes from HBM)."""
     import torch
 
     out = {}
@@ -449,11 +510,11 @@ def copy_probe(sizes_mb=(7, 14, 21), steps: int = 200) -> dict:
         n = mb * (1 << 20) // 4
         R = max(4, REPLICA_BYTES // (n * 4))
         src = [torch.randn(n, device="cuda") for _ in range(R)]
-        dst = [torch.empty(n, device="cuda") for _ in range(R)]
+        dst = torch.empty((), device="cuda")
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
-                dst[i % R].copy_(src[i % R])
+                torch.sum(src[i % R], dim=0, out=dst)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -466,7 +527,7 @@ def copy_probe(sizes_mb=(7, 14, 21), steps: int = 200) -> dict:
         out[f"{mb}MiB"] = {"us": round(us, 2), "read_GBs": round(n * 4 / us / 1e3, 1)}
         del src, dst, g
         torch.cuda.empty_cache()
-    log(f"plain copy probe: {out}")
+    log(f"plain read probe: {out}")
     return out
 
 
@@ -504,16 +565,13 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
     wl = synth.WORKLOADS[args.workload]
-    b, ms, stats, roof, U, dist = measure(wl, args.steps, args.warmup, args.eager, "hbm", args.stages)
-    host0 = b.host0
-    b.close()
-    del b
-    torch.cuda.empty_cache()
-    value = wl.tokens / (ms * 1e-3)
-    step_bytes = U * wl.expert_bytes
+    m = measure(wl, args.steps, args.warmup, args.eager, args.stages, dist=not args.no_steps_dist)
+    host0 = m["host0"]
+    ms = m["ms"]
+    sl = step_line(wl, m)
     line = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(wl.tokens / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -522,43 +580,44 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": wl.name, "hidden": wl.hidden, "experts": wl.experts, "top_k": wl.top_k,
                    "moe_intermediate": wl.inter, "tokens": wl.tokens, "replicas": replicas_for(wl),
+                   "input_pool": X_POOL if wl.tokens <= POOL_MAX_T else 1,
                    "timing": "eager" if args.eager else "hip-graph"},
-        "hbm_step": {"routed_expert_bytes": int(step_bytes), "achieved": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-                     "unit": "GB/s", "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "distinct_experts": U},
-        "roofline": roof,
-        "step_us": dist,
+        "hbm_step": {"routed_expert_bytes": sl["hbm_step"]["routed_expert_bytes"],
+                     "achieved": sl["hbm_step"]["achieved_gbs"], "unit": "GB/s",
+                     "frac": sl["hbm_step"]["frac"], "cold_frac": sl["hbm_step"].get("cold_frac"),
+                     "distinct_experts": m["U"], "experts_touched": m["touched"]},
+        "roofline": m["roofs"][0] if m["roofs"] else None,
+        "other_rooflines": m["roofs"][1:],
     }
+    if "step_us" in sl:
+        line["step_us"] = sl["step_us"]
     if not args.no_prefill:
         pw = synth.WORKLOADS[args.prefill_workload]
-        pb, pms, pstats, proof, pU, pdist = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager,
-                                             "mfma", args.stages)
-        pb.close()
-        del pb
-        torch.cuda.empty_cache()
-        flops = 2.0 * pw.tokens * pw.top_k * 3 * pw.hidden * pw.inter + 2.0 * pw.tokens * pw.experts * pw.hidden
-        line["prefill"] = {
-            "workload": pw.name, "tokens": pw.tokens, "steps": args.prefill_steps, "ms_per_step": round(pms, 4),
-            "tokens_per_s": round(pw.tokens / (pms * 1e-3), 1),
-            "tflops": round(flops / (pms * 1e-3) / 1e12, 2),
-            "frac_mfma_peak": round(flops / (pms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-            "distinct_experts": pU, "max_tokens_per_expert": max(st[1] for st in pstats),
-            "gemm_rows": sum(st[2] for st in pstats) / len(pstats), "roofline": proof, "step_us": pdist,
-        }
+        pm = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager, args.stages,
+                     dist=not args.no_steps_dist)
+        pl = step_line(pw, pm)
+        line["prefill"] = dict(pl, steps=args.prefill_steps, tflops=pl["mfma_step"]["algorithmic_tflops"],
+                               frac_mfma_peak=pl["mfma_step"]["frac"], gemm_rows=pm["gemm_rows"],
+                               roofline=pm["roofs"][0] if pm["roofs"] else None)
     if not args.no_block:
         line["block"] = [measure_block(wl, args.steps, args.eager)]
         if not args.no_prefill:
             line["block"].append(measure_block(synth.WORKLOADS[args.prefill_workload], args.prefill_steps, args.eager))
-    if wl.tokens <= 4:
+    if wl.tokens <= 4 and not args.no_q8:
         line["q8_activations"] = measure_q8(wl, args.steps, args.eager)
-    line["hbm_step"]["plain_copy_probe"] = copy_probe()
+    if not args.no_probe:
+        line["hbm_step"]["plain_read_probe"] = read_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]
     if extras:
-        line["others"] = [measure_step(synth.WORKLOADS[w], args.extra_steps, args.eager, args.stages) for w in extras]
+        line["others"] = []
+        for name in extras:
+            ow = synth.WORKLOADS[name]
+            om = measure(ow, args.extra_steps, max(3, args.extra_steps // 10), args.eager, args.stages, dist=False)
+            line["others"].append(dict(step_line(ow, om), steps=args.extra_steps))
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {wl.name} for ~{args.cpu_seconds:.0f} s")
         line["cpu_baseline"] = cpu_baseline(host0, args.cpu_seconds)

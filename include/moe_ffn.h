@@ -125,8 +125,8 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
  * max |v|, q = rint(v * (127 / amax)) in [-127, 127], d = amax / 127, all in
  * fp32; the router runs on the fp32 x. Arguments, outputs and errors as
  * moe_ffn_forward; this variant covers the decode path only (T <= 4 and the
- * shapes that path takes: hidden_dim <= 4096, num_experts <= 128,
- * num_experts_per_tok * moe_intermediate / 256 <= 48), else INVALID_SHAPE.
+ * shapes that path takes: hidden_dim <= 4096, num_experts <= 256,
+ * num_experts_per_tok * moe_intermediate / 256 <= 384), else INVALID_SHAPE.
  * Non-finite inputs give unspecified outputs. */
 moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                               int32_t *router_idx, void *stream);
@@ -148,8 +148,10 @@ moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *s
  * standard RMSNorm; the pages name the op without its formula), rounded to
  * fp32 as the layer's input, and the residual add of the block after the MoE
  * FFN (forward_qwen3_moe.rs: the "Residual" step after prefill step 2g,
- * decode step 2i). The norm is a launch of its own; the residual add happens
- * in the kernel that writes out.
+ * decode step 2i). On the decode path (T <= 4 and the shapes listed for
+ * moe_ffn_forward_q8) the norm is fused into the router launch; otherwise it
+ * is a launch of its own ahead of the layer. The residual add happens in the
+ * kernel that writes out.
  *   hidden      [T][H] fp32 residual stream.
  *   out         [T][H] fp32 block output. Must not overlap hidden.
  *   router_out, router_idx, stream: as for moe_ffn_forward (routing of the

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 from .build import LIB
@@ -254,6 +255,25 @@ class MoeFfn:
         self.moe_intermediate = moe_intermediate
         self.handle = moe_ffn_create(hidden_dim, num_experts, num_experts_per_tok, moe_intermediate, gate_q4k,
                                      up_q4k, down_q4k, router_w, router_bias, stream)
+
+    @classmethod
+    def from_host(cls, hidden_dim, num_experts, num_experts_per_tok, moe_intermediate, gate_q4k, up_q4k, down_q4k,
+                  router_w, router_bias=None, device="cuda", stream=None):
+        """Create the layer from host arrays (numpy or CPU tensors): the Q4_K blobs as uint8 bytes, the router
+        weight and bias as float32. They are copied to the device for moe_ffn_create, which copies them again into
+        the layer's own layout; the uploads are released when this returns."""
+        def up(a, dt):
+            t = a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))
+            if t.dtype != dt:
+                raise TypeError(f"expected {dt}, got {t.dtype}")
+            return t.reshape(-1).to(device) if dt == torch.uint8 else t.contiguous().to(device)
+
+        g, u, d = up(gate_q4k, torch.uint8), up(up_q4k, torch.uint8), up(down_q4k, torch.uint8)
+        rw = up(router_w, torch.float32)
+        rb = None if router_bias is None else up(router_bias, torch.float32)
+        layer = cls(hidden_dim, num_experts, num_experts_per_tok, moe_intermediate, g, u, d, rw, rb, stream)
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+        return layer
 
     def reserve(self, max_tokens: int, stream=None) -> None:
         moe_ffn_reserve(self.handle, max_tokens, stream)

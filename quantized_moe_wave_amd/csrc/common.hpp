@@ -41,16 +41,15 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
 __device__ __forceinline__ f16x2 u32_as_f16x2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
 __device__ __forceinline__ uint32_t f16x2_as_u32(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
-// Cross-workgroup hand-off without cache maintenance. Data handed to another
-// workgroup of the same launch is written with agent-scope atomic stores and
-// read with agent-scope atomic loads (coherent accesses on this multi-XCD
-// part), so no L2 writeback/invalidate (what a device-wide fence costs) is
-// needed: the writer only waits until its stores have completed before it
-// bumps the completion counter.
+// Cross-workgroup hand-off within one launch. Data handed to another
+// workgroup is written with agent-scope atomic stores and read with
+// agent-scope atomic loads (coherent accesses on this multi-XCD part); the
+// writers wait until their stores have completed, and the completion counter
+// is updated with release/acquire semantics at agent scope.
 __device__ __forceinline__ void wait_own_stores() { __builtin_amdgcn_s_waitcnt(0); }
 
-__device__ __forceinline__ uint32_t counter_arrive(uint32_t *c) {
-    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint32_t counter_arrive_acq_rel(uint32_t *c) {
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // LDS writes of this wave visible to its other lanes: wait for LDS operations

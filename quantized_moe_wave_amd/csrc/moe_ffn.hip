@@ -184,6 +184,7 @@ struct moe_ffn_s {
     Workspace ws;
     int last_T = 0;
     bool last_decode = false;  // whether the most recent forward took the decode path (h rows in pair order)
+    Workspace *last_ws = nullptr;  // workspace of the most recent forward
     Profiler prof;
 };
 
@@ -293,11 +294,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 template <int TT, int EV>
-void launch_router(moe_ffn_t h, int T, const float *x, int32_t *idx, float *w, hipStream_t st) {
+void launch_router(moe_ffn_t h, Workspace &ws, Profiler &pf, int T, const float *x, int32_t *idx, float *w,
+                   hipStream_t st) {
     const moe_ffn_shape &s = h->sh;
     dim3 grid((T + TT - 1) / TT, (s.num_experts + 4 * EV - 1) / (4 * EV));
-    launch(h->prof, kStRouter, router_kernel<TT, EV>, grid, dim3(256), st, x, h->rw, h->rb, T, s.hidden_dim,
-           s.num_experts, s.num_experts_per_tok, h->ws.logits, idx, w, h->ws.rcount);
+    launch(pf, kStRouter, router_kernel<TT, EV>, grid, dim3(256), st, x, h->rw, h->rb, T, s.hidden_dim,
+           s.num_experts, s.num_experts_per_tok, ws.logits, idx, w, ws.rcount);
 }
 
 // Argument checks shared by the forward entry points (x is the layer's input,
@@ -306,7 +308,7 @@ moe_status check_call(moe_ffn_t h, int32_t T, const float *x, float *out, float 
     if (!h) return fail(MOE_ERR_INVALID_ARG, "handle is NULL");
     if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "token count must be >= 1 (got %d)", T);
     const moe_ffn_shape &s = h->sh;
-    const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
+    const int k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
     // staged rows are addressed with 32-bit half offsets
     if ((uint64_t)T * 2 * H >= (1ull << 32) || (uint64_t)T * k * 2 * I >= (1ull << 32))
         return fail(MOE_ERR_INVALID_SHAPE, "token count %d too large for this layer (T*2*H and T*k*2*I must be < 2^32)",
@@ -338,19 +340,18 @@ bool decode_path(const moe_ffn_shape &s, int T) {
 // applies the block's RMSNorm (weight norm_w, eps) to every value it reads.
 // q8 (decode path only): the experts' matvecs take Q8_K-style codes of x and h
 // (stage_row_sb and down_combine_small_kernel stage the codes instead).
-moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out, int32_t *router_idx,
-                         const float *resid, const float *norm_w, double eps, int q8, hipStream_t st) {
+// w: the workspace of this call, laid out for at least T tokens (the handle's
+// own, or the no-alloc variant's scratch); pf: the stage profiler to use.
+moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, const float *x, float *out,
+                         float *router_out, int32_t *router_idx, const float *resid, const float *norm_w, double eps,
+                         int q8, hipStream_t st) {
     const moe_ffn_shape &s = h->sh;
     const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
-    moe_status r = ensure_ws(h, T, st);
-    if (r != MOE_OK) return r;
-    Workspace &w = h->ws;
     int32_t *idx = router_idx ? router_idx : w.idx;
     float *wt = router_out ? router_out : w.w;
     const int S = T * k;
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
-    Profiler &pf = h->prof;
     if ((norm_w || q8) && !decode_path(s, T))
         return fail(MOE_ERR_INVALID_ARG, "internal: fused norm or Q8_K staging off the decode path");
     if (decode_path(s, T)) {
@@ -366,13 +367,14 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
         if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
         h->last_T = T;
         h->last_decode = true;
+        h->last_ws = &w;
         return MOE_OK;
     }
     bool staged_x = false;
     if (T == 1) {
-        launch_router<1, 1>(h, T, x, idx, wt, st);
+        launch_router<1, 1>(h, w, pf, T, x, idx, wt, st);
     } else if (T <= 4) {
-        launch_router<4, 1>(h, T, x, idx, wt, st);
+        launch_router<4, 1>(h, w, pf, T, x, idx, wt, st);
     } else {
         // few token tiles: split H over more workgroups (partials summed in
         // split order by the top-k kernel); ks*T*E stays below kRlPartDoubles
@@ -464,6 +466,7 @@ moe_status forward_layer(moe_ffn_t h, int32_t T, const float *x, float *out, flo
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));
     h->last_T = T;
     h->last_decode = false;
+    h->last_ws = &w;
     return MOE_OK;
 }
 
@@ -561,8 +564,10 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
                            int32_t *router_idx, void *stream) {
     g_err.clear();
     moe_status r = check_call(h, T, x, out, router_out, router_idx);
+    if (r == MOE_OK) r = ensure_ws(h, T, (hipStream_t)stream);
     if (r != MOE_OK) return r;
-    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 0, (hipStream_t)stream);
+    return forward_layer(h, h->ws, h->prof, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 0,
+                         (hipStream_t)stream);
 }
 
 moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
@@ -575,7 +580,10 @@ moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out
                     "the Q8_K-activation variant covers the decode path only (at most %d tokens, hidden_dim <= %d, "
                     "num_experts <= %d, num_experts_per_tok * moe_intermediate / 256 <= %d); got T = %d",
                     kSmallT, kSmallMaxH, kRankMaxExperts, kMaxTopK * 6, T);
-    return forward_layer(h, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 1, (hipStream_t)stream);
+    r = ensure_ws(h, T, (hipStream_t)stream);
+    if (r != MOE_OK) return r;
+    return forward_layer(h, h->ws, h->prof, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 1,
+                         (hipStream_t)stream);
 }
 
 moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *stream) {
@@ -606,15 +614,15 @@ moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, fl
     if (r != MOE_OK) return r;
     if (!h->norm_w) return fail(MOE_ERR_INVALID_ARG, "no norm weight on this handle (call moe_ffn_set_norm first)");
     hipStream_t st = (hipStream_t)stream;
-    // decode path: the norm is fused into its router launch
-    if (decode_path(h->sh, T))
-        return forward_layer(h, T, hidden, out, router_out, router_idx, hidden, h->norm_w, (double)h->norm_eps, 0,
-                             st);
     r = ensure_ws(h, T, st);
     if (r != MOE_OK) return r;
+    // decode path: the norm is fused into its router launch
+    if (decode_path(h->sh, T))
+        return forward_layer(h, h->ws, h->prof, T, hidden, out, router_out, router_idx, hidden, h->norm_w,
+                             (double)h->norm_eps, 0, st);
     launch(h->prof, kStNorm, rmsnorm_kernel, dim3(T), dim3(256), st, hidden, h->norm_w, h->sh.hidden_dim,
            (double)h->norm_eps, h->ws.xn);
-    return forward_layer(h, T, h->ws.xn, out, router_out, router_idx, hidden, nullptr, 0.0, 0, st);
+    return forward_layer(h, h->ws, h->prof, T, h->ws.xn, out, router_out, router_idx, hidden, nullptr, 0.0, 0, st);
 }
 
 moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, int32_t *offsets, int32_t *entries,
@@ -627,10 +635,11 @@ moe_status moe_ffn_debug_routing(moe_ffn_t h, double *logits, int32_t *counts, i
         return fail(MOE_ERR_INVALID_ARG, "debug outputs must be device pointers");
     hipStream_t st = (hipStream_t)stream;
     const size_t T = h->last_T, E = h->sh.num_experts, k = h->sh.num_experts_per_tok;
-    if (logits) HIP_TRY(hipMemcpyAsync(logits, h->ws.logits, T * E * 8, hipMemcpyDeviceToDevice, st));
-    if (counts) HIP_TRY(hipMemcpyAsync(counts, h->ws.counts, E * 4, hipMemcpyDeviceToDevice, st));
-    if (offsets) HIP_TRY(hipMemcpyAsync(offsets, h->ws.offsets, (E + 1) * 4, hipMemcpyDeviceToDevice, st));
-    if (entries) HIP_TRY(hipMemcpyAsync(entries, h->ws.entries, T * k * 4, hipMemcpyDeviceToDevice, st));
+    const Workspace &w = *h->last_ws;
+    if (logits) HIP_TRY(hipMemcpyAsync(logits, w.logits, T * E * 8, hipMemcpyDeviceToDevice, st));
+    if (counts) HIP_TRY(hipMemcpyAsync(counts, w.counts, E * 4, hipMemcpyDeviceToDevice, st));
+    if (offsets) HIP_TRY(hipMemcpyAsync(offsets, w.offsets, (E + 1) * 4, hipMemcpyDeviceToDevice, st));
+    if (entries) HIP_TRY(hipMemcpyAsync(entries, w.entries, T * k * 4, hipMemcpyDeviceToDevice, st));
     return MOE_OK;
 }
 
@@ -644,8 +653,9 @@ moe_status moe_ffn_debug_stats(moe_ffn_t h, int32_t token, const float *out, con
     if (!is_device_ptr(out) || !is_device_ptr(stats) || (router_out && !is_device_ptr(router_out)))
         return fail(MOE_ERR_INVALID_ARG, "out, stats and router_out must be device pointers");
     const moe_ffn_shape &s = h->sh;
-    hipLaunchKernelGGL(stage_stats_kernel, dim3(kStatStages), dim3(256), 0, (hipStream_t)stream, h->ws.logits,
-                       router_out ? router_out : h->ws.w, h->ws.h, h->last_decode ? nullptr : h->ws.pos, out,
+    const Workspace &w = *h->last_ws;
+    hipLaunchKernelGGL(stage_stats_kernel, dim3(kStatStages), dim3(256), 0, (hipStream_t)stream, w.logits,
+                       router_out ? router_out : w.w, w.h, h->last_decode ? nullptr : w.pos, out,
                        (int)token, s.num_experts, s.num_experts_per_tok, s.moe_intermediate, s.hidden_dim, stats);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(e));

@@ -280,12 +280,19 @@ __global__ __launch_bounds__(256) void router_kernel(const float *__restrict__ x
         }
     }
 
-    // Last workgroup of this token group does the selection.
+    // Last workgroup of this token group does the selection. Hand-off: every
+    // wave waits until its logit stores have completed, the barrier orders
+    // them before thread 0's counter update, which is a release at agent scope
+    // (and an acquire, for the workgroup that arrives last); that workgroup's
+    // threads pass the barrier and an agent-scope acquire fence before they
+    // read the logits, so every other workgroup's stores happen before those
+    // reads.
     wait_own_stores();
     __syncthreads();
-    if (tid == 0) s_last = (counter_arrive(&counters[blockIdx.x]) == gridDim.y - 1);
+    if (tid == 0) s_last = (counter_arrive_acq_rel(&counters[blockIdx.x]) == gridDim.y - 1);
     __syncthreads();
     if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     __shared__ __attribute__((aligned(16))) double tk_lds[4][kRankMaxExperts + kMaxTopK + kMaxTopK / 2];
     for (int t = wave; t < nt; t += 4)

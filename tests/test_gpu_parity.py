@@ -1,8 +1,8 @@
 """GPU parity of the HIP layer (through the C ABI) against the fp64 oracle.
 
-Every workload at its full size; the two large ones compare a seeded sample of
-tokens element by element (router, bucket layout and logits are compared for
-all tokens). Edge cases: ragged token counts across tile boundaries, one
+Every workload at its full size, every output element of every token compared
+with the oracle (the two large ones also have a fast sampled variant). Edge
+cases: ragged token counts across tile boundaries, one
 expert taking every token, k = E, zero input, wide dynamic range, workspace
 growth, bitwise run-to-run determinism, and the ABI's error returns.
 """
@@ -51,7 +51,7 @@ def _run(inp, layer, x):
     return inp2, g
 
 
-@pytest.mark.parametrize("name", ["tiny", "30b-decode", "30b-batch"])
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_workload_full(name):
     print(f"[parity] workload {name} full", flush=True)
     inp, layer, dev = _layer(name)
@@ -63,6 +63,7 @@ def test_workload_full(name):
 
 @pytest.mark.parametrize("name,nsample", [("30b-prefill", 48), ("235b-shape", 40)])
 def test_workload_sampled(name, nsample):
+    """Fast variant of the full check on a seeded sample of tokens."""
     print(f"[parity] workload {name} sampled", flush=True)
     inp, layer, dev = _layer(name)
     g = parity.run_gpu(layer, dev["x"])
