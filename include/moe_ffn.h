@@ -48,8 +48,9 @@
 extern "C" {
 #endif
 
-/* 2: adds moe_ffn_set_norm, moe_ffn_forward_block, moe_ffn_debug_stats and moe_ffn_forward_q8. */
-#define MOE_FFN_ABI_VERSION 2
+/* 2: adds moe_ffn_set_norm, moe_ffn_forward_block, moe_ffn_debug_stats and moe_ffn_forward_q8.
+ * 3: adds moe_ffn_forward_noalloc. */
+#define MOE_FFN_ABI_VERSION 3
 
 typedef struct moe_ffn_s *moe_ffn_t;
 
@@ -116,6 +117,25 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
  * overlapping x, bad handle), OOM, DEVICE. */
 moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                            int32_t *router_idx, void *stream);
+
+/* moe_ffn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, outputs, results (bit for bit) and errors as
+ * moe_ffn_forward, but the per-call workspace is a fixed scratch array of 64
+ * MiB that the library holds on each device from its load until the process
+ * ends, instead of the handle's own workspace: the call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine) and never grows
+ * anything. Its limit is the token count whose workspace fits 64 MiB (about
+ * 490 tokens at hidden 2048, 128 experts, top-8, intermediate 768); a larger
+ * T returns INVALID_SHAPE naming the limit, before anything is enqueued. Every
+ * call on one device shares that device's scratch and leaves its contents
+ * there: calls that overlap on one device (several streams, or several host
+ * threads, whatever the handle) race, so the caller orders them, e.g. on one
+ * stream. moe_ffn_debug_routing and moe_ffn_debug_stats after this call read
+ * the shared scratch, valid until the next no-alloc call on the device. The
+ * current device must be the handle's (else INVALID_ARG). */
+moe_status moe_ffn_forward_noalloc(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                                   int32_t *router_idx, void *stream);
 
 /* The layer with Q8_K-style int8 activations for the routed experts (the
  * activation format of the production CPU path in qwen3_moe_dispatch.rs, doc

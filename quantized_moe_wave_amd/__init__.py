@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     moe_ffn_destroy,
     moe_ffn_forward,
     moe_ffn_forward_block,
+    moe_ffn_forward_noalloc,
     moe_ffn_forward_q8,
     moe_ffn_profile,
     moe_ffn_profile_read,

@@ -39,6 +39,8 @@ _lib.moe_ffn_reserve.argtypes = [_vp, ctypes.c_int32, _vp]
 _lib.moe_ffn_reserve.restype = ctypes.c_int
 _lib.moe_ffn_forward.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_forward.restype = ctypes.c_int
+_lib.moe_ffn_forward_noalloc.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
+_lib.moe_ffn_forward_noalloc.restype = ctypes.c_int
 _lib.moe_ffn_forward_q8.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp]
 _lib.moe_ffn_forward_q8.restype = ctypes.c_int
 _lib.moe_ffn_set_norm.argtypes = [_vp, _vp, ctypes.c_float, _vp]
@@ -141,6 +143,22 @@ def moe_ffn_forward(handle: int, x: torch.Tensor, out: torch.Tensor, router_out:
     st = _lib.moe_ffn_forward(_vp(handle), int(x.shape[0]), _ptr(x), _ptr(out), _ptr(router_out), _ptr(router_idx),
                               _stream(stream))
     _check(st, "moe_ffn_forward")
+
+
+def moe_ffn_forward_noalloc(handle: int, x: torch.Tensor, out: torch.Tensor, router_out: torch.Tensor | None = None,
+                            router_idx: torch.Tensor | None = None, stream=None) -> None:
+    """moe_ffn_forward on the library's fixed per-device scratch: allocates nothing (T limited by the scratch)."""
+    _dev(x, "x", torch.float32)
+    _dev(out, "out", torch.float32)
+    if x.dim() != 2 or out.shape != x.shape:
+        raise ValueError("x and out must both be [T, hidden_dim]")
+    if router_out is not None:
+        _dev(router_out, "router_out", torch.float32)
+    if router_idx is not None:
+        _dev(router_idx, "router_idx", torch.int32)
+    st = _lib.moe_ffn_forward_noalloc(_vp(handle), int(x.shape[0]), _ptr(x), _ptr(out), _ptr(router_out),
+                                      _ptr(router_idx), _stream(stream))
+    _check(st, "moe_ffn_forward_noalloc")
 
 
 def moe_ffn_forward_q8(handle: int, x: torch.Tensor, out: torch.Tensor, router_out: torch.Tensor | None = None,
@@ -282,6 +300,10 @@ class MoeFfn:
         if out is None:
             out = torch.empty_like(x)
         moe_ffn_forward(self.handle, x, out, router_out, router_idx, stream)
+        return out
+
+    def forward_noalloc(self, x, out, router_out=None, router_idx=None, stream=None):
+        moe_ffn_forward_noalloc(self.handle, x, out, router_out, router_idx, stream)
         return out
 
     def forward_q8(self, x, out=None, router_out=None, router_idx=None, stream=None):

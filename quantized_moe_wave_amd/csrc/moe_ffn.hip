@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -184,11 +185,44 @@ struct moe_ffn_s {
     Workspace ws;
     int last_T = 0;
     bool last_decode = false;  // whether the most recent forward took the decode path (h rows in pair order)
-    Workspace *last_ws = nullptr;  // workspace of the most recent forward
+    Workspace *last_ws = nullptr;  // workspace of the most recent forward (ws, or scratch_ws)
     Profiler prof;
+    uint8_t *scratch = nullptr;    // this device's copy of the no-alloc scratch (device address)
+    Workspace scratch_ws;          // layout of the most recent no-alloc forward over it
 };
 
+// Scratch of moe_ffn_forward_noalloc: the workspace of every call of that
+// entry point on a device, so that it allocates nothing. Each device holds its
+// own copy of the array (from the library's load until the process ends); in
+// host code its name is only a stand-in, and the device address of this
+// device's copy comes from hipGetSymbolAddress (scratch_address, called once
+// per device by moe_ffn_create with that device current).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (dev: the current device).
+hipError_t scratch_address(int dev, uint8_t **out) {
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_addr[dev] = (uint8_t *)p;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
 
 bool is_device_ptr(const void *p) {
     if (!p) return false;
@@ -530,6 +564,12 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
             return cleanup(fail(MOE_ERR_DEVICE, "hipGetDeviceProperties failed"));
         h->cus_per_xcd = prop.multiProcessorCount % 8 == 0 ? prop.multiProcessorCount / 8 : 0;
     }
+    {
+        const hipError_t e = scratch_address(h->device, &h->scratch);
+        if (e != hipSuccess)
+            return cleanup(fail(MOE_ERR_DEVICE, "hipGetSymbolAddress of the no-alloc scratch failed on device %d: %s",
+                                h->device, hipGetErrorString(e)));
+    }
     const int E = s.num_experts, H = s.hidden_dim, I = s.moe_intermediate;
     if (hipMalloc(&h->gu, 2 * gb) != hipSuccess || hipMalloc(&h->dn, db) != hipSuccess ||
         hipMalloc(&h->rw, (size_t)E * H * 4) != hipSuccess ||
@@ -568,6 +608,37 @@ moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, f
     if (r != MOE_OK) return r;
     return forward_layer(h, h->ws, h->prof, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 0,
                          (hipStream_t)stream);
+}
+
+moe_status moe_ffn_forward_noalloc(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
+                                   int32_t *router_idx, void *stream) {
+    g_err.clear();
+    moe_status r = check_call(h, T, x, out, router_out, router_idx);
+    if (r != MOE_OK) return r;
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != h->device)
+        return fail(MOE_ERR_INVALID_ARG, "the current device (%d) is not the handle's device (%d)", dev, h->device);
+    Workspace w;
+    const size_t need = layout_ws(h->sh, T, nullptr, &w);
+    if (need > kScratchBytes) {
+        int tmax = T;
+        while (tmax > 1 && layout_ws(h->sh, tmax, nullptr, &w) > kScratchBytes) tmax = tmax * 3 / 4;
+        while (layout_ws(h->sh, tmax + 1, nullptr, &w) <= kScratchBytes) ++tmax;
+        return fail(MOE_ERR_INVALID_SHAPE,
+                    "T = %d needs %zu bytes of scratch; the no-alloc variant has %zu (at most %d tokens of this layer)",
+                    T, need, kScratchBytes, layout_ws(h->sh, 1, nullptr, &w) <= kScratchBytes ? tmax : 0);
+    }
+    layout_ws(h->sh, T, (char *)h->scratch, &w);
+    h->scratch_ws = w;
+    hipStream_t st = (hipStream_t)stream;
+    // the router's completion counters (used by router_kernel, T <= 4 off the
+    // decode path) must start at zero: clear them, whatever an earlier call
+    // left in the shared scratch
+    if (T <= 4 && !decode_path(h->sh, T)) zero_u32_kernel<<<1, 256, 0, st>>>(h->scratch_ws.rcount, T);
+    static Profiler no_profile;  // never enabled: no events are created or recorded
+    return forward_layer(h, h->scratch_ws, no_profile, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 0,
+                         st);
 }
 
 moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(b):
 
 
 def test_abi_version(b):
-    assert b.abi_version() == 2
+    assert b.abi_version() == 3
 
 
 def _shape(b, H=256, E=8, k=2, I=256):
