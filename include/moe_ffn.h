@@ -169,9 +169,11 @@ moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *s
  * fp32 as the layer's input, and the residual add of the block after the MoE
  * FFN (forward_qwen3_moe.rs: the "Residual" step after prefill step 2g,
  * decode step 2i). On the decode path (T <= 4 and the shapes listed for
- * moe_ffn_forward_q8) the norm is fused into the router launch; otherwise it
- * is a launch of its own ahead of the layer. The residual add happens in the
- * kernel that writes out.
+ * moe_ffn_forward_q8) the norm is fused into the router launch; on the
+ * bucketed path (T > 4) into the router and top-k launches when
+ * num_experts <= 256 and hidden_dim <= 4096; otherwise it is a launch of its
+ * own ahead of the layer. The residual add happens in the kernel that writes
+ * out.
  *   hidden      [T][H] fp32 residual stream.
  *   out         [T][H] fp32 block output. Must not overlap hidden.
  *   router_out, router_idx, stream: as for moe_ffn_forward (routing of the
@@ -219,13 +221,15 @@ moe_status moe_ffn_debug_stats(moe_ffn_t h, int32_t token, const float *out, con
 
 /* Per-stage GPU timing for benchmarks. Stages of one forward, in launch order:
  * 0 router (logits, and for at most 4 tokens also the top-k), 1 topk (which
- * also stages x when num_experts <= 256), 2 bucket, 3 stage_x (when the top-k
+ * also stages x when num_experts <= 256), 2 bucket (the per-chunk expert
+ * histogram; 13 bucket_scatter places the pairs), 3 stage_x (when the top-k
  * launch does not stage x), 4 gate_up (16-row tiles of buckets of at most 16 entries, or the
  * per-pair decode kernel), 5 gate_up_big (tiles of up to 64 rows for larger
  * buckets), 6 stage_h, 7 down (16-row tiles, or the fused decode down +
  * combine), 8 down_big, 9 combine, 10 gate_up_tail and 11 down_tail (the
  * 64-row GEMMs' last-round tiles as half-width units), 12 norm (the RMSNorm of
- * moe_ffn_forward_block); a stage a forward does not run has no
+ * moe_ffn_forward_block, where it is a launch of its own), 13 bucket_scatter;
+ * a stage a forward does not run has no
  * launches (moe_ffn_stage_name gives the name, moe_ffn_stage_count the number).
  * moe_ffn_profile sets a bit mask of stages; while it is non-zero, each forward
  * records a HIP event on its stream right before and right after every

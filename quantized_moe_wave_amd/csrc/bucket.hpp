@@ -15,10 +15,18 @@
 // (e, first entry, rows, 0), in expert order. n_tiles[0] = number of small
 // tiles, n_tiles[1] = number of GEMM tiles.
 //
-// Grid: E workgroups (one per expert), 256 threads. Every workgroup builds the
-// full histogram in LDS (integer atomics only), so no workgroup waits for
-// another. Each thread holds runs of kBkPairs consecutive pairs in registers,
-// loaded in one go, so a round costs one memory round trip.
+// Two launches over chunks of kBkChunk consecutive pairs (one pair per
+// thread), with integer arithmetic only:
+//   bucket_hist_kernel     the expert histogram of each chunk -> hist[chunk][E]
+//   bucket_scatter_kernel  each chunk: totals and its prefix over earlier
+//                          chunks from hist, the exclusive scan over experts,
+//                          and the place of each of its pairs: the earlier
+//                          pairs of the same expert in earlier chunks, in
+//                          earlier waves of the chunk, and in lower lanes of
+//                          the wave (lanes with equal keys found by ballots);
+//                          chunk 0 also writes counts, offsets and the tiles.
+// No workgroup reads all pairs, and no counter is contended by a hot expert
+// (a wave adds one count per distinct expert it holds).
 #pragma once
 #include "common.hpp"
 #include "gemm.hpp"
@@ -29,137 +37,164 @@ namespace moe {
 __device__ __forceinline__ int gemm_tiles_of(int c) { return c >= kGemmMinRows ? (c + kGemmM - 1) / kGemmM : 0; }
 __device__ __forceinline__ int small_tiles_of(int c) { return c >= kGemmMinRows ? 0 : (c + kTileM - 1) / kTileM; }
 
-constexpr int kBkPairs = 32;  // consecutive (token, slot) pairs per thread per round
+constexpr int kBkChunk = 256;  // pairs per chunk = threads per workgroup
+constexpr int kBkLoads = 16;   // histogram entries a thread has in flight
+constexpr int kBkKeyBits = 11; // keys 0..kMaxExperts (kMaxExperts: "no pair")
+static_assert(kMaxExperts < (1 << kBkKeyBits), "keys must fit the ballot match");
 
-__global__ __launch_bounds__(256) void bucket_kernel(const int32_t *__restrict__ idx, int T, int k, int E,
-                                                     int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-                                                     int32_t *__restrict__ entries, int32_t *__restrict__ pos,
-                                                     int4 *__restrict__ tiles, int4 *__restrict__ big_tiles,
-                                                     int32_t *__restrict__ n_tiles) {
-    __shared__ int cnt[kMaxExperts];
-    __shared__ int red[3][4];
-    __shared__ int wave_tot[2][4];
+__host__ __device__ inline int bucket_chunks(int S) { return (S + kBkChunk - 1) / kBkChunk; }
+
+// Lanes of this wave whose key equals this lane's (every lane must call it).
+__device__ __forceinline__ uint64_t lanes_with_key(uint32_t key) {
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int b = 0; b < kBkKeyBits; ++b) {
+        const uint32_t bit = (key >> b) & 1u;
+        const uint64_t set = __ballot(bit);
+        m &= bit ? set : ~set;
+    }
+    return m;
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+    const int lane = threadIdx.x & 63;
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Exclusive scan over n <= 4 * 256 values v[0..n) in LDS by a 256-thread
+// workgroup (thread t owns v[t*per .. t*per + per), per = ceil(n / 256)):
+// out[i] = sum of v below i (out may alias v); returns the total. Two barriers.
+__device__ __forceinline__ int block_scan_lds(const int *v, int *out, int n, int *red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int e = blockIdx.x;
-    const int S = T * k;
-    constexpr int kRound = 256 * kBkPairs;
+    const int per = (n + 255) / 256;
+    int loc[4] = {0, 0, 0, 0};
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = tid * per + i;
+        if (i < per && j < n) loc[i] = v[j];
+        sum += loc[i];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += red[w];
+    const int total = red[0] + red[1] + red[2] + red[3];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = tid * per + i;
+        if (i < per && j < n) out[j] = run;
+        run += loc[i];
+    }
+    __syncthreads();
+    return total;
+}
 
-    // this thread's pairs of a round, loaded together (16 bytes at a time
-    // where aligned; pairs past S read as -1)
-    const bool vec_ok = ((uintptr_t)idx & 15u) == 0;  // the caller's array may be only 4-byte aligned
-    auto load_pairs = [&](int r0, int (&v)[kBkPairs]) {
-        const int s0 = r0 + tid * kBkPairs;
+// Grid: bucket_chunks(S) workgroups of kBkChunk threads.
+__global__ __launch_bounds__(kBkChunk) void bucket_hist_kernel(const int32_t *__restrict__ idx, int S, int E,
+                                                              int32_t *__restrict__ hist) {
+    __shared__ int cnt[kMaxExperts];
+    const int tid = threadIdx.x;
+    const int s = blockIdx.x * kBkChunk + tid;
+    const uint32_t key = s < S ? (uint32_t)idx[s] : (uint32_t)kMaxExperts;
+    for (int e = tid; e < E; e += kBkChunk) cnt[e] = 0;
+    __syncthreads();
+    const uint64_t m = lanes_with_key(key);
+    if (key < (uint32_t)E && (m & lanes_below()) == 0) atomicAdd(&cnt[key], __popcll(m));
+    __syncthreads();
+    for (int e = tid; e < E; e += kBkChunk) hist[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Grid: bucket_chunks(S) workgroups of kBkChunk threads.
+__global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
+    const int32_t *__restrict__ idx, int S, int E, const int32_t *__restrict__ hist, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ entries, int32_t *__restrict__ pos, int4 *__restrict__ tiles,
+    int4 *__restrict__ big_tiles, int32_t *__restrict__ n_tiles) {
+    __shared__ int tot[kMaxExperts];   // pairs per expert
+    __shared__ int base[kMaxExperts];  // its first entry, then + pairs of earlier chunks
+    __shared__ int wcnt[4][kMaxExperts];
+    __shared__ int red[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int chunk = blockIdx.x, nchunks = gridDim.x;
+    const int s = chunk * kBkChunk + tid;
+    // this thread's pair and its lanes of equal key, ahead of the hist reads
+    const uint32_t key = s < S ? (uint32_t)idx[s] : (uint32_t)kMaxExperts;
+    for (int e = tid; e < E; e += kBkChunk) {
+        tot[e] = 0;
+        base[e] = 0;
 #pragma unroll
-        for (int i = 0; i < kBkPairs; i += 4) {
-            if (vec_ok && s0 + i + 3 < S) {
-                const int4 q = *(const int4 *)&idx[s0 + i];
-                v[i] = q.x;
-                v[i + 1] = q.y;
-                v[i + 2] = q.z;
-                v[i + 3] = q.w;
-            } else {
+        for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
+    }
+    __syncthreads();
+    // totals and the prefix over earlier chunks: for E <= 256 the 256 / E
+    // threads of expert e take every (256 / E)-th chunk, kBkLoads loads in
+    // flight per thread, and add their sums in LDS (integer atomics); more
+    // experts loop over them
+    const int tpe = E <= kBkChunk ? kBkChunk / E : 1;
+    if (tid < tpe * E) {
+        for (int e = tid % E; e < E; e += kBkChunk) {
+            int sum_t = 0, sum_p = 0;
+            for (int c0 = tid / E * (E <= kBkChunk); c0 < nchunks; c0 += tpe * kBkLoads) {
+                int v[kBkLoads];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) v[i + j] = s0 + i + j < S ? idx[s0 + i + j] : -1;
+                for (int i = 0; i < kBkLoads; ++i) {
+                    const int c = c0 + i * tpe;
+                    v[i] = c < nchunks ? hist[(size_t)c * E + e] : 0;
+                }
+#pragma unroll
+                for (int i = 0; i < kBkLoads; ++i) {
+                    sum_t += v[i];
+                    sum_p += c0 + i * tpe < chunk ? v[i] : 0;
+                }
             }
-        }
-    };
-
-    for (int i = tid; i < E; i += 256) cnt[i] = 0;
-    __syncthreads();
-    for (int r0 = 0; r0 < S; r0 += kRound) {
-        int v[kBkPairs];
-        load_pairs(r0, v);
-#pragma unroll
-        for (int i = 0; i < kBkPairs; ++i)
-            if (v[i] >= 0) atomicAdd(&cnt[v[i]], 1);
-    }
-    __syncthreads();
-
-    // Entries and tiles below expert e.
-    int below = 0, tiles_below = 0, big_below = 0, tiles_all = 0, big_all = 0;
-    for (int i = tid; i < E; i += 256) {
-        const int c = cnt[i];
-        const int nb = gemm_tiles_of(c);
-        const int ns = small_tiles_of(c);
-        tiles_all += ns;
-        big_all += nb;
-        if (i < e) {
-            below += c;
-            tiles_below += ns;
-            big_below += nb;
+            atomicAdd(&tot[e], sum_t);
+            atomicAdd(&base[e], sum_p);
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        below += __shfl_xor(below, o, kWave);
-        tiles_below += __shfl_xor(tiles_below, o, kWave);
-        big_below += __shfl_xor(big_below, o, kWave);
-        tiles_all += __shfl_xor(tiles_all, o, kWave);
-        big_all += __shfl_xor(big_all, o, kWave);
-    }
-    if (lane == 0) {
-        red[0][wave] = below;
-        red[1][wave] = tiles_below;
-        red[2][wave] = big_below;
-        wave_tot[0][wave] = tiles_all;
-        wave_tot[1][wave] = big_all;
-    }
+    const uint64_t m = lanes_with_key(key);
+    if (key < (uint32_t)E && (m & lanes_below()) == 0) wcnt[wave][key] = __popcll(m);
     __syncthreads();
-    const int off = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const int toff = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    const int boff = red[2][0] + red[2][1] + red[2][2] + red[2][3];
-    const int mine = cnt[e];
-    const int nbig = gemm_tiles_of(mine);
-    const int nsmall = small_tiles_of(mine);
+    // first entry of every expert: exclusive scan of the totals
+    __shared__ int off_l[kMaxExperts];
+    block_scan_lds(tot, off_l, E, red);
+    if (key < (uint32_t)E) {
+        int r = __popcll(m & lanes_below());
+        for (int w = 0; w < wave; ++w) r += wcnt[w][key];
+        const int p = off_l[key] + base[key] + r;
+        entries[p] = s;
+        pos[s] = p;
+    }
+    if (chunk != 0) return;
+    // chunk 0: counts, offsets and the tile lists (wcnt is reused once every
+    // thread has placed its pair)
+    __syncthreads();
+    for (int e = tid; e < E; e += kBkChunk) {
+        counts[e] = tot[e];
+        offsets[e] = off_l[e];
+        wcnt[0][e] = small_tiles_of(tot[e]);
+        wcnt[1][e] = gemm_tiles_of(tot[e]);
+    }
+    if (tid == 0) offsets[E] = S;
+    __syncthreads();
+    const int ns = block_scan_lds(wcnt[0], wcnt[2], E, red);
+    const int nb = block_scan_lds(wcnt[1], wcnt[3], E, red);
+    for (int e = tid; e < E; e += kBkChunk) {
+        const int c = tot[e], off = off_l[e];
+        const int nsm = small_tiles_of(c), nbg = gemm_tiles_of(c);
+        for (int i = 0; i < nbg; ++i)
+            big_tiles[wcnt[3][e] + i] = make_int4(e, off + i * kGemmM, min(kGemmM, c - i * kGemmM), 0);
+        for (int i = 0; i < nsm; ++i)
+            tiles[wcnt[2][e] + i] = make_int4(e, off + i * kTileM, min(kTileM, c - i * kTileM), 0);
+    }
     if (tid == 0) {
-        counts[e] = mine;
-        offsets[e] = off;
-        if (e == E - 1) offsets[E] = off + mine;
-        if (e == 0) {
-            n_tiles[0] = wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
-            n_tiles[1] = wave_tot[1][0] + wave_tot[1][1] + wave_tot[1][2] + wave_tot[1][3];
-        }
-    }
-    for (int i = tid; i < nbig; i += 256)
-        big_tiles[boff + i] = make_int4(e, off + i * kGemmM, min(kGemmM, mine - i * kGemmM), 0);
-    for (int i = tid; i < nsmall; i += 256)
-        tiles[toff + i] = make_int4(e, off + i * kTileM, min(kTileM, mine - i * kTileM), 0);
-    if (mine == 0) return;
-
-    // Stable scatter: pairs in index order (= token order, a token choosing e
-    // at most once). Each thread counts e among its consecutive pairs, a
-    // workgroup scan places them, and the thread writes its matches in order.
-    __syncthreads();  // wave_tot is reused below
-    int base = off;
-    for (int r0 = 0; r0 < S; r0 += kRound) {
-        int v[kBkPairs];
-        load_pairs(r0, v);
-        int m = 0;
-#pragma unroll
-        for (int i = 0; i < kBkPairs; ++i) m += (int)(v[i] == e);
-        int incl = m;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += y;
-        }
-        if (lane == 63) wave_tot[0][wave] = incl;
-        __syncthreads();
-        int before = incl - m;
-        for (int w = 0; w < wave; ++w) before += wave_tot[0][w];
-        const int total = wave_tot[0][0] + wave_tot[0][1] + wave_tot[0][2] + wave_tot[0][3];
-        int p = base + before;
-        const int s0 = r0 + tid * kBkPairs;
-#pragma unroll
-        for (int i = 0; i < kBkPairs; ++i) {
-            if (v[i] == e) {
-                entries[p] = s0 + i;
-                pos[s0 + i] = p;
-                ++p;
-            }
-        }
-        base += total;
-        __syncthreads();  // wave_tot is rewritten by the next round
+        n_tiles[0] = ns;
+        n_tiles[1] = nb;
     }
 }
 

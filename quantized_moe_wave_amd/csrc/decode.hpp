@@ -375,14 +375,17 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
     const int e = sel_e[p - t * k];
     const uint8_t *wg = GU + (size_t)((size_t)e * ngroups + rg) * nsb * kGroupSbBytes;
 
-    // wave w takes super-blocks w, w + kGpWaves, ...; two per pass
+    // wave w takes super-blocks w, w + kGpWaves, ...; two per pass (the
+    // second only where it exists: the condition is uniform over the wave)
     auto load_pass = [&](int b0, u32x4 (&q0)[2], u32x4 (&q1)[2], u32x4 (&hd)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const uint8_t *blk = wg + (size_t)min(b0 + kGpWaves * i, nsb - 1) * kGroupSbBytes;
-            q0[i] = *(const u32x4 *)(blk + lane * 16);
-            q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
-            hd[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
+            if (i == 0 || b0 + kGpWaves * i < nsb) {
+                const uint8_t *blk = wg + (size_t)min(b0 + kGpWaves * i, nsb - 1) * kGroupSbBytes;
+                q0[i] = *(const u32x4 *)(blk + lane * 16);
+                q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
+                hd[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
+            }
         }
     };
     // the weight loads go out as soon as the expert is known, ahead of the

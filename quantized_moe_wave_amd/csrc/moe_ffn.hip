@@ -4,7 +4,8 @@
 // forward(T) enqueues, all on the caller's stream, with no host wait:
 //   1. router_kernel   logits (fp64), top-k, renormalised weights (a few
 //                      tokens), or router_logits_kernel + topk_kernel
-//   2. bucket_kernel   stable counting sort of (token, slot) by expert + tiles
+//   2. bucket_hist_kernel, bucket_scatter_kernel: stable counting sort of
+//                      (token, slot) by expert + tiles
 //   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums
 //   4. expert GATEUP   gate/up Q4_K MFMA + SiLU(g)*u -> h[slot][I]
 //   5. stage_kernel    h rows -> staged
@@ -78,6 +79,7 @@ struct Workspace {
     int4 *tiles = nullptr;        // [max tiles] 16-row tiles
     int4 *big_tiles = nullptr;    // [max_gemm_tiles] GEMM tiles (up to 64 rows)
     int32_t *n_tiles = nullptr;   // [2] small, big
+    int32_t *hist = nullptr;      // [bucket_chunks(S)][E] per-chunk expert histogram
     f16 *x_hilo = nullptr;        // [T][2H]
     f16 *x_xs = nullptr;          // [T][H/256][16]
     float *x_sinv = nullptr;      // [T][H/256]
@@ -110,11 +112,12 @@ enum Stage {
     kStGateUpTail,
     kStDownTail,
     kStNorm,
+    kStBucketScatter,
     kStCount
 };
 const char *const kStageNames[kStCount] = {"router",      "topk",    "bucket",   "stage_x",  "gate_up",
                                            "gate_up_big", "stage_h", "down",     "down_big", "combine",
-                                           "gate_up_tail", "down_tail", "norm"};
+                                           "gate_up_tail", "down_tail", "norm", "bucket_scatter"};
 
 // Start/stop events of profiled stages. A profiled kernel is launched with
 // hipExtLaunchKernelGGL, which timestamps the kernel's own start and end.
@@ -282,6 +285,7 @@ size_t layout_ws(const moe_ffn_shape &s, int cap, char *base, Workspace *w) {
     w->tiles = (int4 *)take((size_t)max_tiles((int)S, (int)E) * sizeof(int4));
     w->big_tiles = (int4 *)take((size_t)max_gemm_tiles((int)S, (int)E) * sizeof(int4));
     w->n_tiles = (int32_t *)take(8);
+    w->hist = (int32_t *)take((size_t)bucket_chunks((int)S) * E * 4);
     w->x_hilo = (f16 *)take(T * 2 * H * 2);
     w->x_xs = (f16 *)take(T * nh * 16 * 2);
     w->x_sinv = (float *)take(T * nh * 4);
@@ -368,6 +372,14 @@ bool decode_path(const moe_ffn_shape &s, int T) {
     return T <= kSmallT && H <= kSmallMaxH && E <= kRankMaxExperts && k * ni <= kMaxTopK * 6;
 }
 
+// Whether the block's RMSNorm folds into the general path's router and top-k
+// launches: the MFMA router with the rank top-k after it, and rows that fit
+// the top-k wave's registers.
+bool fold_norm_general(const moe_ffn_shape &s, int T) {
+    const int nh = s.hidden_dim / kQ4Weights;
+    return T > 4 && s.num_experts <= kRankMaxExperts && (nh + 1) / 2 <= kStageRegPairs;
+}
+
 // The layer on T tokens of x (already checked); resid, if not null, is added
 // to the output by the kernel that writes it (the block's residual add).
 // norm_w (decode path only): x is the residual stream and the router launch
@@ -386,8 +398,10 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
     const int S = T * k;
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
-    if ((norm_w || q8) && !decode_path(s, T))
-        return fail(MOE_ERR_INVALID_ARG, "internal: fused norm or Q8_K staging off the decode path");
+    if (q8 && !decode_path(s, T))
+        return fail(MOE_ERR_INVALID_ARG, "internal: Q8_K staging off the decode path");
+    if (norm_w && !decode_path(s, T) && !fold_norm_general(s, T))
+        return fail(MOE_ERR_INVALID_ARG, "internal: fused norm where the router cannot take it");
     if (decode_path(s, T)) {
         // decode path: three launches (see decode.hpp)
         launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
@@ -421,25 +435,32 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
         if (E <= kRankMaxExperts)
             while (ks < kRlMaxSplit && rtiles * ks < 128 && (H / (64 * nwv)) % (2 * ks) == 0) ks *= 2;
         const dim3 rgrid((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks);
+        // with the block's norm folded in, the router leaves 1/rms and the
+        // bias to the top-k launch
+        const float *rbias = norm_w ? nullptr : h->rb;
         if (nwv == 8)
-            launch(pf, kStRouter, router_logits_kernel<8>, rgrid, dim3(512), st, x, h->rw, h->rb, T, H, E, w.logits,
-                   ks, w.lpart);
+            launch(pf, kStRouter, norm_w ? router_logits_kernel<8, true> : router_logits_kernel<8, false>, rgrid,
+                   dim3(512), st, x, h->rw, rbias, T, H, E, w.logits, ks, w.lpart, norm_w);
         else
-            launch(pf, kStRouter, router_logits_kernel<4>, rgrid, dim3(256), st, x, h->rw, h->rb, T, H, E, w.logits,
-                   ks, w.lpart);
+            launch(pf, kStRouter, norm_w ? router_logits_kernel<4, true> : router_logits_kernel<4, false>, rgrid,
+                   dim3(256), st, x, h->rw, rbias, T, H, E, w.logits, ks, w.lpart, norm_w);
         if (E <= kRankMaxExperts) {
-            // the top-k launch also stages x
-            auto topk = E <= 64 ? topk_kernel<1> : E <= 128 ? topk_kernel<2> : topk_kernel<4>;
+            // the top-k launch also stages x (normalised, with the block's norm)
+            auto topk = norm_w ? (E <= 64 ? topk_kernel<1, true> : E <= 128 ? topk_kernel<2, true> : topk_kernel<4, true>)
+                               : (E <= 64 ? topk_kernel<1, false> : E <= 128 ? topk_kernel<2, false>
+                                                                              : topk_kernel<4, false>);
             launch(pf, kStTopk, topk, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks, w.lpart, x, H,
-                   w.x_hilo, w.x_xs, w.x_sinv);
+                   w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, norm_w ? h->rb : nullptr);
             staged_x = true;
         } else {
             launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
         }
     }
 
-    launch(pf, kStBucket, bucket_kernel, dim3(E), dim3(256), st, idx, T, k, E, w.counts, w.offsets, w.entries, w.pos,
-           w.tiles, w.big_tiles, w.n_tiles);
+    const int nchunks = bucket_chunks(S);
+    launch(pf, kStBucket, bucket_hist_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist);
+    launch(pf, kStBucketScatter, bucket_scatter_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist,
+           w.counts, w.offsets, w.entries, w.pos, w.tiles, w.big_tiles, w.n_tiles);
 
     if (!staged_x)
         launch(pf, kStStageX, stage_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
@@ -687,8 +708,9 @@ moe_status moe_ffn_forward_block(moe_ffn_t h, int32_t T, const float *hidden, fl
     hipStream_t st = (hipStream_t)stream;
     r = ensure_ws(h, T, st);
     if (r != MOE_OK) return r;
-    // decode path: the norm is fused into its router launch
-    if (decode_path(h->sh, T))
+    // decode path: the norm is fused into its router launch; general path:
+    // into the router and top-k launches (where they can take it)
+    if (decode_path(h->sh, T) || fold_norm_general(h->sh, T))
         return forward_layer(h, h->ws, h->prof, T, hidden, out, router_out, router_idx, hidden, h->norm_w,
                              (double)h->norm_eps, 0, st);
     launch(h->prof, kStNorm, rmsnorm_kernel, dim3(T), dim3(256), st, hidden, h->norm_w, h->sh.hidden_dim,

@@ -19,6 +19,7 @@
 // the softmax/top-k for that group's tokens, one wave per token.
 #pragma once
 #include "common.hpp"
+#include "norm.hpp"
 #include "stage.hpp"
 
 namespace moe {
@@ -333,12 +334,18 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 constexpr int kRlMaxSplit = 16;
 constexpr int kRlPartDoubles = 256 * 1024;  // ks*T*E < 1024 * 256 for the ks the host picks
 
-template <int NWV>
+// NORM (the block's pre-FFN RMSNorm folded in, norm_w = its weight g): the
+// kernel sums W_r[e] . (x * g) (each product x*g exact in double) and leaves
+// the row's 1/rms factor, and the bias, to topk_kernel, which has the row:
+// logit = (1/rms) * sum + bias. Equal to the sum over the rounded normalised
+// row up to the rounding of its elements (a few 1e-8 of a logit).
+template <int NWV, bool NORM>
 __global__ __launch_bounds__(64 * NWV) void router_logits_kernel(const float *__restrict__ x,
                                                                  const float *__restrict__ wr,
                                                                  const float *__restrict__ bias, int T, int H, int E,
                                                                  double *__restrict__ logits, int ks,
-                                                                 double *__restrict__ part_out) {
+                                                                 double *__restrict__ part_out,
+                                                                 const float *__restrict__ norm_w) {
     __shared__ double part[NWV][2][2][4][64];  // [wave][token block][expert block][element][lane]
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -362,33 +369,37 @@ __global__ __launch_bounds__(64 * NWV) void router_logits_kernel(const float *__
         for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
     // register ring of kRlPf groups: group j sits in slot j % kRlPf
-    float4 ra[kRlPf][2], rb[kRlPf][2];
-    auto load_grp = [&](int j, float4 (&a)[2], float4 (&b)[2]) {
+    const float *gcol = NORM ? norm_w + kbeg + 4 * g : nullptr;
+    float4 ra[kRlPf][2], rb[kRlPf][2], rg[kRlPf];
+    auto load_grp = [&](int j, float4 (&a)[2], float4 (&b)[2], float4 &gg) {
         const int jj = min(j, ngrp - 1);  // past the end: reload the last group (unused)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             a[t] = *(const float4 *)(xr[t] + 16 * jj);
             b[t] = *(const float4 *)(wrow[t] + 16 * jj);
         }
+        if (NORM) gg = *(const float4 *)(gcol + 16 * jj);
     };
 #pragma unroll
-    for (int j = 0; j < kRlPf; ++j) load_grp(j, ra[j], rb[j]);
+    for (int j = 0; j < kRlPf; ++j) load_grp(j, ra[j], rb[j], rg[j]);
 
     for (int j0 = 0; j0 < ngrp; j0 += kRlPf) {
 #pragma unroll
         for (int u = 0; u < kRlPf; ++u) {
-            const float4 a0 = ra[u][0], a1 = ra[u][1], b0 = rb[u][0], b1 = rb[u][1];
-            load_grp(j0 + u + kRlPf, ra[u], rb[u]);
+            const float4 a0 = ra[u][0], a1 = ra[u][1], b0 = rb[u][0], b1 = rb[u][1], g0 = rg[u];
+            load_grp(j0 + u + kRlPf, ra[u], rb[u], rg[u]);
             const float av[2][4] = {{a0.x, a0.y, a0.z, a0.w}, {a1.x, a1.y, a1.z, a1.w}};
             const float bv[2][4] = {{b0.x, b0.y, b0.z, b0.w}, {b1.x, b1.y, b1.z, b1.w}};
+            const float gv[4] = {g0.x, g0.y, g0.z, g0.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
                     for (int eb = 0; eb < 2; ++eb)
-                        acc[tb][eb] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)av[tb][i], (double)bv[eb][i],
-                                                                          acc[tb][eb], 0, 0, 0);
+                        acc[tb][eb] = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                            NORM ? (double)av[tb][i] * (double)gv[i] : (double)av[tb][i], (double)bv[eb][i],
+                            acc[tb][eb], 0, 0, 0);
         }
     }
 
@@ -426,17 +437,31 @@ __global__ __launch_bounds__(64 * NWV) void router_logits_kernel(const float *__
 // the grouped GEMM, as stage_kernel would (independent of the routing); the
 // row's loads are issued right after the logits' and land while the
 // selection runs.
-template <int PL>
+// NORM (router_logits_kernel<.., true> ran before; x then holds the block's
+// residual stream, whose row must fit the registers; norm_w is the norm
+// weight): the wave computes its
+// row's 1/rms r from the row it stages, turns each sum into the logit
+// r * sum + bias (written back for the debug copy) and stages the normalised
+// row fp32(x * g * r) (products in double, as rmsnorm_kernel).
+template <int PL, bool NORM>
 __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
                                                    const double *__restrict__ part, const float *__restrict__ x,
                                                    int H, f16 *__restrict__ x_hilo, f16 *__restrict__ x_xs,
-                                                   float *__restrict__ x_sinv) {
+                                                   float *__restrict__ x_sinv, const float *__restrict__ norm_w,
+                                                   double eps, const float *__restrict__ bias) {
     __shared__ __attribute__((aligned(16))) double tk_lds[4][64 * PL + kMaxTopK + kMaxTopK / 2];
     __shared__ __attribute__((aligned(16))) double sums[4][64 * PL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
+    const int nh = H / kQ4Weights;
+    const bool row_in_regs = x && (nh + 1) / 2 <= kStageRegPairs;
+    StagedRow sr;
+    // the row's 1/rms first (it scales every logit), from a pass of its own
+    // over the row, so that the row is held in registers only from the
+    // selection on, as without the norm
+    const double r = NORM ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
     const double *lrow = logits + (size_t)t * E;
     if (ks > 1) {
         for (int c = lane; c < E; c += 64) {
@@ -448,6 +473,15 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
 #pragma unroll
             for (int z = 1; z < kRlMaxSplit; ++z)
                 if (z < ks) v += pv[z];
+            if (NORM) v = r * v + (bias ? (double)bias[c] : 0.0);
+            sums[wave][c] = v;
+            logits[(size_t)t * E + c] = v;
+        }
+        lds_wave_sync();
+        lrow = sums[wave];
+    } else if (NORM) {
+        for (int c = lane; c < E; c += 64) {
+            const double v = r * lrow[c] + (bias ? (double)bias[c] : 0.0);
             sums[wave][c] = v;
             logits[(size_t)t * E + c] = v;
         }
@@ -456,11 +490,14 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
     }
     double lv[PL];
     topk_rank_load<PL, false>(lrow, E, lv);
-    const int nh = H / kQ4Weights;
-    const bool row_in_regs = x && (nh + 1) / 2 <= kStageRegPairs;
-    StagedRow sr;
     if (row_in_regs) stage_row_load(x + (size_t)t * H, nh, sr);
     topk_rank_select<PL>(lv, E, k, idx_out + (size_t)t * k, w_out + (size_t)t * k, nullptr, tk_lds[wave]);
+    if (NORM) {  // the weight row only now, so that it does not stay live across the selection
+        asm volatile("" ::: "memory");
+        StagedRow gr;
+        stage_row_load(norm_w, nh, gr);
+        staged_row_normalise(sr, gr, nh, r);
+    }
     if (row_in_regs)
         stage_row_store(sr, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16, x_sinv + (size_t)t * nh);
     else if (x)

@@ -175,6 +175,29 @@ __device__ __forceinline__ void stage_emit(int b, float4 a, float4 c, float sc, 
     }
 }
 
+// The block's RMSNorm on a row loaded by stage_row_load, with its weight gr
+// (loaded the same way) and 1/rms r: each value becomes fp32(x * g * r), the
+// products in double.
+__device__ __forceinline__ void staged_row_normalise(StagedRow &sr, const StagedRow &gr, int nsb, double r) {
+    const int npairs = (nsb + 1) >> 1;
+    auto nz = [&](float4 &v, const float4 &g) {
+        v.x = (float)((double)v.x * g.x * r);
+        v.y = (float)((double)v.y * g.y * r);
+        v.z = (float)((double)v.z * g.z * r);
+        v.w = (float)((double)v.w * g.w * r);
+    };
+    // pair by pair (a scheduling fence between pairs), so that the double
+    // intermediates of one pair only are live at a time
+#pragma unroll
+    for (int p = 0; p < kStageRegPairs; ++p) {
+        if (p < npairs) {
+            nz(sr.va[p], gr.va[p]);
+            nz(sr.vb[p], gr.vb[p]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Scale and store a row loaded by stage_row_load.
 __device__ __forceinline__ void stage_row_store(const StagedRow &sr, int nsb, f16 *__restrict__ hilo_row,
                                                 f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
