@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
     __shared__ int base[kMaxExperts];  // its first entry, then + pairs of earlier chunks
     __shared__ int wcnt[4][kMaxExperts];
     __shared__ int red[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int chunk = blockIdx.x, nchunks = gridDim.x;
     const int s = chunk * kBkChunk + tid;
     // this thread's pair and its lanes of equal key, ahead of the hist reads
