@@ -27,8 +27,10 @@ The layer inside its block (moe_ffn_forward_block: pre-FFN RMSNorm, the layer, r
 add) is timed the same way on the decode and prefill workloads under "block", with the
 time of one per-stage statistics call (moe_ffn_debug_stats) on the last token.
 
-The decode layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8) is timed
-the same way under "q8_activations".
+The layer with Q8_K-style int8 expert activations (moe_ffn_forward_q8) is timed the
+same way under "q8_activations": the decode step, and the prefill step with its own
+grouped-GEMM roofline (one MFMA pass on the codes; flops counted as for the exact
+layer) and its speedup over the exact prefill step.
 
 The 64-token batch and the 235b-shaped layer are timed as whole steps, each with
 the roofline of its own dominant kernels, under "others". For context,
@@ -333,6 +335,8 @@ def kernel_roofline(b: Bench, steps: int, kind: str) -> dict | None:
     import quantized_moe_wave_amd as q
 
     stages, bound, pkey = KERNELS[kind]
+    if b.q8:
+        pkey += " on Q8_K codes"  # a kernel of its own: no stored counters apply
     stages = [s for s in stages if s in q.moe_ffn_stage_names()]
     got = b.stage_times(steps, stages)
     total_ms = sum(got[s][0] for s in stages)
@@ -382,18 +386,20 @@ def log_stages(b: Bench, steps: int) -> None:
             log(f"{b.wl.name}: stage {s:12s} {tm / n * 1e3:9.2f} us avg over {n} launches")
 
 
-def measure(wl, steps: int, warmup: int, eager: bool, want_stages: bool, dist: bool = True) -> dict:
-    """Step time, the roofline of the workload's kernels, the experts touched, and the single-step distribution."""
+def measure(wl, steps: int, warmup: int, eager: bool, want_stages: bool, dist: bool = True,
+            q8: bool = False) -> dict:
+    """Step time, the roofline of the workload's kernels, the experts touched, and the single-step distribution
+    (q8: of moe_ffn_forward_q8)."""
     import torch
 
-    b = Bench(wl, replicas_for(wl))
+    b = Bench(wl, replicas_for(wl), q8=q8)
     try:
         b.routing()
         ms = b.timed(steps, warmup, eager)
         st = [b.step_stats(i) for i in range(steps)]
         U = sum(s["U"] for s in st) / steps
         touched = b.touched(steps)
-        log(f"{wl.name}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'}); "
+        log(f"{wl.name}{' q8' if q8 else ''}: {ms * 1e3:.2f} us/step over {steps} steps ({'eager' if eager else 'graph'}); "
             f"mean U {U:.1f}; experts touched over the loop {touched}")
         roofs = [r for r in (kernel_roofline(b, steps, k) for k in kinds_for(b)) if r]
         if want_stages:
@@ -607,8 +613,18 @@ def main() -> int:
         line["block"] = [measure_block(wl, args.steps, args.eager)]
         if not args.no_prefill:
             line["block"].append(measure_block(synth.WORKLOADS[args.prefill_workload], args.prefill_steps, args.eager))
-    if wl.tokens <= 4 and not args.no_q8:
-        line["q8_activations"] = measure_q8(wl, args.steps, args.eager)
+    if not args.no_q8:
+        q8s = []
+        if wl.tokens <= 4:
+            q8s.append(measure_q8(wl, args.steps, args.eager))
+        if not args.no_prefill:
+            qm = measure(pw, args.prefill_steps, max(3, args.prefill_steps // 10), args.eager, args.stages,
+                         dist=False, q8=True)
+            ql = step_line(pw, qm)
+            q8s.append(dict(ql, steps=args.prefill_steps, tflops=ql["mfma_step"]["algorithmic_tflops"],
+                            frac_mfma_peak=ql["mfma_step"]["frac"], speedup_vs_exact=round(pm["ms"] / qm["ms"], 3),
+                            roofline=qm["roofs"][0] if qm["roofs"] else None))
+        line["q8_activations"] = q8s
     if not args.no_probe:
         line["hbm_step"]["plain_read_probe"] = read_probe()
     extras = [w for w in args.extra_workloads.split(",") if w]

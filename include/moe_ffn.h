@@ -143,11 +143,11 @@ moe_status moe_ffn_forward_noalloc(moe_ffn_t h, int32_t T, const float *x, float
  * forward's): each token's x row and each expert's h
  * enter the expert matvecs as codes q and a scale d per 256 values, amax =
  * max |v|, q = rint(v * (127 / amax)) in [-127, 127], d = amax / 127, all in
- * fp32; the router runs on the fp32 x. Arguments, outputs and errors as
- * moe_ffn_forward; this variant covers the decode path only (T <= 4 and the
- * shapes that path takes: hidden_dim <= 4096, num_experts <= 256,
- * num_experts_per_tok * moe_intermediate / 256 <= 384), else INVALID_SHAPE.
- * Non-finite inputs give unspecified outputs. */
+ * fp32; the router runs on the fp32 x. Arguments, outputs, token counts and
+ * errors as moe_ffn_forward (the same paths: a decode path for T <= 4 and the
+ * bucketed grouped GEMMs, there in one MFMA pass on the codes, each output in
+ * units of the row's d per super-block). Non-finite inputs give unspecified
+ * outputs. */
 moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                               int32_t *router_idx, void *stream);
 

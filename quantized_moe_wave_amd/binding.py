@@ -163,7 +163,7 @@ def moe_ffn_forward_noalloc(handle: int, x: torch.Tensor, out: torch.Tensor, rou
 
 def moe_ffn_forward_q8(handle: int, x: torch.Tensor, out: torch.Tensor, router_out: torch.Tensor | None = None,
                        router_idx: torch.Tensor | None = None, stream=None) -> None:
-    """out[T][H] <- MoE FFN of x with Q8_K-style int8 expert activations (decode path: T <= 4)."""
+    """out[T][H] <- MoE FFN of x with Q8_K-style int8 expert activations (codes and a scale per 256 values)."""
     _dev(x, "x", torch.float32)
     _dev(out, "out", torch.float32)
     if x.dim() != 2 or out.shape != x.shape:

@@ -71,7 +71,10 @@ constexpr int kGemmRing = 4;              // A chunk buffers
 static_assert(kGemmRing == 4, "ring slot of chunk 4b + q is q");
 
 // Tile shape: RB 16-row blocks, CW 16-column weight groups per wave, NW waves.
-template <int RB, int CW, int NW>
+// Q8: the activations are Q8_K-style codes with a scale per row and
+// super-block (one MFMA pass, and each wave keeps the tile rows' scales of
+// the current and the next super-block).
+template <int RB, int CW, int NW, bool Q8 = false>
 struct GemmShape {
     static_assert(NW == 4 || NW == 8, "4 or 8 waves");
     static constexpr int M = 16 * RB;                       // rows per tile
@@ -85,8 +88,11 @@ struct GemmShape {
     // load 16 (rows 32*(wave%2) + lane/2; waves 2, 3 repeat waves 0, 1)
     static constexpr int XsBuf = NW == 8 ? 2048 : 4096;
     static constexpr int HLoads = HdrBuf / (NW * 1024) + 1;  // headers + the k-step sums
-    static constexpr size_t SvOff =
+    static constexpr int DxBuf = Q8 ? NW * 256 : 0;          // Q8: 64 rows' scales, one copy per wave
+    static constexpr int HxLoads = HLoads + (Q8 ? 1 : 0);    // loads of one HX group
+    static constexpr size_t DxOff =
         (size_t)kGemmRing * ABuf + 2 * (size_t)BqBuf + 2 * (size_t)HdrBuf + 2 * (size_t)XsBuf;
+    static constexpr size_t SvOff = DxOff + 2 * (size_t)DxBuf;
     static constexpr size_t Lds = SvOff + NW * 64 * sizeof(float);  // + 1/s of the rows, one copy per wave
     // output staging (after the main loop, over the same LDS): M rows of up to
     // 16 * Groups floats, padded by 4 floats against bank conflicts
@@ -138,22 +144,24 @@ __device__ __forceinline__ float silu_fast(float z) {
 //   slots themselves; out Y[slot][H].
 // tiles[t] = (expert, first bucket slot, rows), t < *n_tiles. ngroups must be
 // a multiple of 4*CW; ncb = ngroups / (4*CW) column blocks; grid = 8 * ncb *
-// ceil(max tiles / 8). a_sinv holds 1/s of every row (nsb equal entries).
+// ceil(max tiles / 8). a_sinv holds 1/s of every row (nsb equal entries);
+// with Q8 the row's Q8_K scale d of every super-block.
 // Main loop of one output tile (everything up to the epilogue). The LDS
 // buffers come in as separate restrict pointers, so the compiler knows which
 // global->LDS load each LDS read depends on and adds no wait of its own
 // beyond the fixed ones below (without that knowledge it drains every load in
 // flight before each header read).
-template <bool GATEUP, int RB, int CW, int NW>
+template <bool GATEUP, int RB, int CW, int NW, bool Q8>
 __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_t *__restrict__ bqbuf,
                                               uint8_t *__restrict__ hbuf, uint8_t *__restrict__ xsbuf,
-                                              float *__restrict__ svbuf, const uint8_t *__restrict__ W, int ngroups,
+                                              float *__restrict__ dxbuf, float *__restrict__ svbuf,
+                                              const uint8_t *__restrict__ W, int ngroups,
                                               int nsb, const int32_t *__restrict__ entries, int k,
                                               const f16 *__restrict__ a_hilo, const f16 *__restrict__ a_xs,
                                               const float *__restrict__ a_sinv, int e, int r0, int rows, int rg0,
                                               int wave, f32x4 (&X)[RB][CW], float (&fcur)[CW]) {
-    using Sh = GemmShape<RB, CW, NW>;
-    constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads;
+    using Sh = GemmShape<RB, CW, NW, Q8>;
+    constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads, kHxLoads = Sh::HxLoads;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
     const int K = nsb * kQ4Weights;
@@ -209,7 +217,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 #pragma unroll
         for (int i = 0; i < kBLoads; ++i) load_lds16(wtile + boff[i] + src, dst + i * 1024);
     };
-    auto issue_hx = [&](int b) {  // headers + k-step sums of super-block b into buffer b % 2   (kHLoads loads)
+    auto issue_hx = [&](int b) {  // headers + k-step sums (+ Q8 row scales) of super-block b into buffer b % 2   (kHxLoads loads)
         uint8_t *dst = hbuf + (b & 1) * Sh::HdrBuf + wave * (kHLoads - 1) * 1024;
 #pragma unroll
         for (int i = 0; i < kHLoads - 1; ++i)
@@ -218,6 +226,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             load_lds4(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 256);
         else
             load_lds16(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 1024);
+        if (Q8)  // the tile rows' scales of super-block b (row lane), one copy per wave
+            load_lds4(a_sinv + (size_t)src_row(lane) * nsb + b, dxbuf + (b & 1) * (Sh::DxBuf / 4) + wave * 64);
     };
 
     // ---- sub-block scales of this lane's CW weight groups (row n) for the
@@ -246,7 +256,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
         for (int rb = 0; rb < RB; ++rb) {
             const int r = rb * 16 + n;  // A row of this lane (r % 16 == n)
             Ah[rb] = *(const f16x8 *)(ab + r * kChunkBytes + jh * 16);
-            Al[rb] = *(const f16x8 *)(ab + r * kChunkBytes + jl * 16);
+            if (!Q8) Al[rb] = *(const f16x8 *)(ab + r * kChunkBytes + jl * 16);  // Q8 codes have no lo part
         }
     };
     // the lane's 16 quant bytes of half super-block hs (chunks 2hs, 2hs + 1:
@@ -299,6 +309,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 #pragma unroll
             for (int cb = 0; cb < CW; ++cb)
                 X[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[rb], Bf[cb], X[rb][cb], 0, 0, 0);
+        if (Q8) return;  // codes are exact in the hi part
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -311,8 +322,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     // steadily instead of in one burst (masks: 0x100 LDS read, 0x008 MFMA,
     // 0x002 VALU, 0x020 global load)
     auto interleave = [&](int nld) {
-        constexpr int kM = 2 * RB * CW;
-        constexpr int kDs = (2 * RB + CW + 1) / 2;
+        constexpr int kM = (Q8 ? 1 : 2) * RB * CW;
+        constexpr int kDs = ((Q8 ? 1 : 2) * RB + CW + 1) / 2;
         constexpr int kValuPer = (CW * 10 + (kM - kDs) - 1) / (kM - kDs) + 1;
         const int every = nld > 0 ? (kM - kDs) / nld : kM;
 #pragma unroll
@@ -336,10 +347,10 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
         for (int j = 0; j < CW; ++j) asm volatile("" : "+v"(Bf[j]));
     };
 
-    // ---- prologue: 1/s of the tile's rows (row lane, one copy per wave),
-    // then the issue groups of iterations -4 .. -1 (nchunks >= 4):
+    // ---- prologue: the tile rows' scale of the last super-block (1/s, or
+    // with Q8 its d; row lane, one copy per wave), then the issue groups of iterations -4 .. -1 (nchunks >= 4):
     // HX(0) A(0) | Bq(0) A(1) | A(2) | Bq(1) A(3)
-    load_lds4(a_sinv + (size_t)src_row(lane) * nsb, svbuf + wave * 64);
+    load_lds4(a_sinv + (size_t)src_row(lane) * nsb + (nsb - 1), svbuf + wave * 64);  // the last super-block's
     issue_hx(0);
     issue_a(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -436,12 +447,31 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 
             // half 0: MFMAs of (c, 2q) from set 0 | fill set 1 with (c, 2q+1)
             if (q == 0) {
+                // Q8: X is also in units of the row's scale D_b (its d, or 1
+                // where d = 0: such a block adds nothing), so the rows' factor
+                // D_{b-1} / D_b joins the columns' (both scales still in LDS:
+                // HX(b+1) refills the older buffer after the next barrier)
+                float fr[RB][4];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) fr[rb][i] = 1.f;
+                if (Q8 && b > 0) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const f32x4 dp = *(const f32x4 *)(dxbuf + ((b - 1) & 1) * (Sh::DxBuf / 4) + wave * 64 + rb * 16 + 4 * g);
+                        const f32x4 dc = *(const f32x4 *)(dxbuf + (b & 1) * (Sh::DxBuf / 4) + wave * 64 + rb * 16 + 4 * g);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            fr[rb][i] = (dp[i] != 0.f ? dp[i] : 1.f) * __builtin_amdgcn_rcpf(dc[i] != 0.f ? dc[i] : 1.f);
+                    }
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int cb = 0; cb < CW; ++cb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) X[rb][cb][i] *= fcur[cb];
+                        for (int i = 0; i < 4; ++i) X[rb][cb][i] *= Q8 ? fcur[cb] * fr[rb][i] : fcur[cb];
             }
             if (q == 1) min_term(b);
             read_a_half(c, 1, Ah1, Al1);
@@ -463,9 +493,9 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
             else if (!LOADS)
                 wait_vm<0>();
             else if (q == 1)
-                wait_vm<2 * kALoads + kHLoads>();
+                wait_vm<2 * kALoads + kHxLoads>();
             else if (q == 2)
-                wait_vm<2 * kALoads + kHLoads + kBLoads>();
+                wait_vm<2 * kALoads + kHxLoads + kBLoads>();
             else
                 wait_vm<2 * kALoads>();
             __builtin_amdgcn_s_waitcnt(0xC07F);  // own LDS reads done before their buffers are refilled
@@ -496,7 +526,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                 issue_a(c + 4);
             }
             mfma_half(Ah1, Al1, B1);
-            interleave(!LOADS ? 0 : q == 0 ? kHLoads + kALoads : q == 2 ? kALoads : kBLoads + kALoads);
+            interleave(!LOADS ? 0 : q == 0 ? kHxLoads + kALoads : q == 2 ? kALoads : kBLoads + kALoads);
             pin(B0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -535,20 +565,21 @@ __device__ __forceinline__ TailSplit tail_split(int ntl, int ncb, int x, int C) 
 template <int RB, int NW>
 constexpr int gemm_waves_per_simd() { return RB == 1 ? 2 : NW / 4; }
 
-template <bool GATEUP, int RB, int CW, int NW>
+template <bool GATEUP, int RB, int CW, int NW, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((
     amdgpu_waves_per_eu(gemm_waves_per_simd<RB, NW>(), gemm_waves_per_simd<RB, NW>()))) void expert_gemm_kernel(
     const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
     const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld, int C,
     int mode) {
-    using Sh = GemmShape<RB, CW, NW>;
+    using Sh = GemmShape<RB, CW, NW, Q8>;
     constexpr int NT = 64 * NW;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t *abuf = smem;
     uint8_t *bqbuf = abuf + kGemmRing * Sh::ABuf;
     uint8_t *hbuf = bqbuf + 2 * Sh::BqBuf;
     uint8_t *xsbuf = hbuf + 2 * Sh::HdrBuf;
+    float *dxbuf = (float *)(smem + Sh::DxOff);
     float *svbuf = (float *)(smem + Sh::SvOff);
 
     // unit of this workgroup (tail_split): mode 0 every unit of this launch,
@@ -579,18 +610,22 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((
 
     f32x4 X[RB][CW];
     float fcur[CW];
-    gemm_mainloop<GATEUP, RB, CW, NW>(abuf, bqbuf, hbuf, xsbuf, svbuf, W, ngroups, nsb, entries, k, a_hilo, a_xs,
+    gemm_mainloop<GATEUP, RB, CW, NW, Q8>(abuf, bqbuf, hbuf, xsbuf, dxbuf, svbuf, W, ngroups, nsb, entries, k, a_hilo, a_xs,
                                       a_sinv, e, r0, rows, rg0, wave, X, fcur);
 
     // results: X of tile rows rb*16 + 4g + i, columns of weight group
-    // CW*wave + cb, times d of the last super-block and the row's 1/s; staged through LDS (once every wave
+    // CW*wave + cb, times d of the last super-block and the row's scale (1/s,
+    // or with Q8 its d of the last super-block); staged through LDS (once every wave
     // is done with the loop's buffers), then written row by row with 16-byte
     // stores (rows past the end of a partial tile are not stored)
     float sv[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[rb][i] = svbuf[wave * 64 + rb * 16 + 4 * g + i];
+        for (int i = 0; i < 4; ++i) {
+            const float v = svbuf[wave * 64 + rb * 16 + 4 * g + i];
+            sv[rb][i] = v != 0.f ? v : 1.f;  // Q8: an all-zero last block has d = 0 (its unit is 1)
+        }
     __syncthreads();
     constexpr int OC = GATEUP ? Sh::Groups * 8 : Sh::Groups * kRowGroup;  // output columns of the tile
     float *stg = (float *)smem;

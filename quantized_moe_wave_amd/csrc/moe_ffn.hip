@@ -380,12 +380,93 @@ bool fold_norm_general(const moe_ffn_shape &s, int T) {
     return T > 4 && s.num_experts <= kRankMaxExperts && (nh + 1) / 2 <= kStageRegPairs;
 }
 
+// Dynamic LDS limits of the grouped GEMM instances (above the default).
+template <bool Q8>
+hipError_t gemm_lds_limits() {
+    const hipError_t a[6] = {
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4, Q8>::Lds)};
+    for (hipError_t e : a)
+        if (e != hipSuccess) return e;
+    return hipSuccess;
+}
+
+// The expert matmuls of the general path: gate/up grouped GEMMs into h, h
+// staged, down grouped GEMMs into Y. Q8: Q8_K-style activation codes (x staged
+// so by the caller, h here), one MFMA pass.
+template <bool Q8>
+void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_t st) {
+    const moe_ffn_shape &s = h->sh;
+    const int E = s.num_experts, k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
+    const int S = T * k;
+    const int nh = H / kQ4Weights, ni = I / kQ4Weights;
+    // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
+    // (see gemm.hpp); 16-row x 256-column tiles (4 waves) for buckets of at
+    // most 16 entries, 64-row x 512-column tiles (8 waves) for larger ones, or
+    // 64 x 256 (4 waves) where the weight groups do not split into blocks of 32.
+    const int gu_groups = I / 8, dn_groups = H / kRowGroup;
+    const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
+    using Small = GemmShape<1, 4, 4, Q8>;
+    using Big = GemmShape<4, 4, 8, Q8>;
+    using BigN = GemmShape<4, 4, 4, Q8>;
+    // big tiles: the 8-wave launch leaves each XCD's split tail units (see
+    // tail_split in gemm.hpp) to a 4-wave launch that runs them as halves;
+    // only where there are enough pairs for several big tiles per XCD (with
+    // few or none the extra launch costs more than it saves)
+    const int C = S >= (size_t)E * kGemmMinRows ? h->cus_per_xcd : 0;
+    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4, 4, Q8>, dim3(8 * (gu_groups / Small::Groups) * ms8),
+               dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
+               w.x_xs, w.x_sinv, w.h, I, 0, 0);
+    if (S >= kGemmMinRows) {
+        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 4, 8, Q8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
+                   dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
+                   w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
+        if (C > 0)
+            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 4, 4, Q8>, dim3(8 * C), dim3(256), BigN::Lds, st,
+                       h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
+                       w.h, I, C, 2);
+    }
+
+    launch(pf, kStStageH, stage_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo, w.h_xs,
+           w.h_sinv, (int)Q8);
+
+    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4, 4, Q8>, dim3(8 * (dn_groups / Small::Groups) * ms8),
+               dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
+               w.h_xs, w.h_sinv, w.Y, H, 0, 0);
+    if (S >= kGemmMinRows) {
+        if (gemm_big_waves(dn_groups) == 8) {
+            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8, Q8>,
+                       dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, C, 1);
+            if (C > 0)
+                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 4, 4, Q8>, dim3(8 * C), dim3(256), BigN::Lds,
+                           st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs,
+                           w.h_sinv, w.Y, H, C, 2);
+        } else {
+            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 4, Q8>,
+                       dim3(8 * (dn_groups / BigN::Groups) * mg8), dim3(256), BigN::Lds, st, h->dn, dn_groups, ni,
+                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, 0, 0);
+        }
+    }
+
+}
+
 // The layer on T tokens of x (already checked); resid, if not null, is added
 // to the output by the kernel that writes it (the block's residual add).
 // norm_w (decode path only): x is the residual stream and the router launch
 // applies the block's RMSNorm (weight norm_w, eps) to every value it reads.
-// q8 (decode path only): the experts' matvecs take Q8_K-style codes of x and h
-// (stage_row_sb and down_combine_small_kernel stage the codes instead).
+// q8: the experts' matvecs take Q8_K-style codes of x and h (the staging
+// launches store the codes instead; the grouped GEMMs run one MFMA pass).
 // w: the workspace of this call, laid out for at least T tokens (the handle's
 // own, or the no-alloc variant's scratch); pf: the stage profiler to use.
 moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, const float *x, float *out,
@@ -398,8 +479,6 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
     const int S = T * k;
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
 
-    if (q8 && !decode_path(s, T))
-        return fail(MOE_ERR_INVALID_ARG, "internal: Q8_K staging off the decode path");
     if (norm_w && !decode_path(s, T) && !fold_norm_general(s, T))
         return fail(MOE_ERR_INVALID_ARG, "internal: fused norm where the router cannot take it");
     if (decode_path(s, T)) {
@@ -450,7 +529,7 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
                                : (E <= 64 ? topk_kernel<1, false> : E <= 128 ? topk_kernel<2, false>
                                                                               : topk_kernel<4, false>);
             launch(pf, kStTopk, topk, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks, w.lpart, x, H,
-                   w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, norm_w ? h->rb : nullptr);
+                   w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, norm_w ? h->rb : nullptr, q8);
             staged_x = true;
         } else {
             launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);
@@ -464,56 +543,12 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
 
     if (!staged_x)
         launch(pf, kStStageX, stage_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,
-               w.x_xs, w.x_sinv);
+               w.x_xs, w.x_sinv, q8);
 
-    // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
-    // (see gemm.hpp); 16-row x 256-column tiles (4 waves) for buckets of at
-    // most 16 entries, 64-row x 512-column tiles (8 waves) for larger ones, or
-    // 64 x 256 (4 waves) where the weight groups do not split into blocks of 32.
-    const int gu_groups = I / 8, dn_groups = H / kRowGroup;
-    const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
-    using Small = GemmShape<1, 4, 4>;
-    using Big = GemmShape<4, 4, 8>;
-    using BigN = GemmShape<4, 4, 4>;
-    // big tiles: the 8-wave launch leaves each XCD's split tail units (see
-    // tail_split in gemm.hpp) to a 4-wave launch that runs them as halves;
-    // only where there are enough pairs for several big tiles per XCD (with
-    // few or none the extra launch costs more than it saves)
-    const int C = S >= (size_t)E * kGemmMinRows ? h->cus_per_xcd : 0;
-    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4, 4>, dim3(8 * (gu_groups / Small::Groups) * ms8),
-               dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
-               w.x_xs, w.x_sinv, w.h, I, 0, 0);
-    if (S >= kGemmMinRows) {
-        launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 4, 8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
-                   dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
-                   w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
-        if (C > 0)
-            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 4, 4>, dim3(8 * C), dim3(256), BigN::Lds, st,
-                       h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
-                       w.h, I, C, 2);
-    }
-
-    launch(pf, kStStageH, stage_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo, w.h_xs,
-           w.h_sinv);
-
-    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4, 4>, dim3(8 * (dn_groups / Small::Groups) * ms8),
-               dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
-               w.h_xs, w.h_sinv, w.Y, H, 0, 0);
-    if (S >= kGemmMinRows) {
-        if (gemm_big_waves(dn_groups) == 8) {
-            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8>,
-                       dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
-                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, C, 1);
-            if (C > 0)
-                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 4, 4>, dim3(8 * C), dim3(256), BigN::Lds,
-                           st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs,
-                           w.h_sinv, w.Y, H, C, 2);
-        } else {
-            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 4>,
-                       dim3(8 * (dn_groups / BigN::Groups) * mg8), dim3(256), BigN::Lds, st, h->dn, dn_groups, ni,
-                       w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, 0, 0);
-        }
-    }
+    if (q8)
+        expert_gemms<true>(h, w, pf, T, st);
+    else
+        expert_gemms<false>(h, w, pf, T, st);
 
     launch(pf, kStCombine, combine_kernel, dim3((H + 1023) / 1024, T), dim3(256), st, w.Y, w.pos, wt, H, k, resid, out);
 
@@ -553,23 +588,11 @@ moe_status moe_ffn_create(const moe_ffn_shape *shape, const void *gate_q4k, size
         return fail(MOE_ERR_INVALID_ARG, "weights must be device pointers");
     hipStream_t hs = (hipStream_t)stream;
     {
-        const hipError_t a[6] = {
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds),
-            hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4>::Lds)};
-        for (hipError_t e : a)
-            if (e != hipSuccess)
-                return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
-                            GemmShape<4, 4, 8>::Lds, hipGetErrorString(e));
+        hipError_t e = gemm_lds_limits<false>();
+        if (e == hipSuccess) e = gemm_lds_limits<true>();
+        if (e != hipSuccess)
+            return fail(MOE_ERR_DEVICE, "cannot raise the GEMM kernels' LDS limit to %zu bytes: %s",
+                        GemmShape<4, 4, 8, true>::Lds, hipGetErrorString(e));
     }
     moe_ffn_t h = new moe_ffn_s();
     h->sh = s;
@@ -667,11 +690,6 @@ moe_status moe_ffn_forward_q8(moe_ffn_t h, int32_t T, const float *x, float *out
     g_err.clear();
     moe_status r = check_call(h, T, x, out, router_out, router_idx);
     if (r != MOE_OK) return r;
-    if (!decode_path(h->sh, T))
-        return fail(MOE_ERR_INVALID_SHAPE,
-                    "the Q8_K-activation variant covers the decode path only (at most %d tokens, hidden_dim <= %d, "
-                    "num_experts <= %d, num_experts_per_tok * moe_intermediate / 256 <= %d); got T = %d",
-                    kSmallT, kSmallMaxH, kRankMaxExperts, kMaxTopK * 6, T);
     r = ensure_ws(h, T, (hipStream_t)stream);
     if (r != MOE_OK) return r;
     return forward_layer(h, h->ws, h->prof, T, x, out, router_out, router_idx, nullptr, nullptr, 0.0, 1,

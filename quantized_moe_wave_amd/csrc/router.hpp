@@ -443,13 +443,14 @@ __global__ __launch_bounds__(64 * NWV) void router_logits_kernel(const float *__
 // row's 1/rms r from the row it stages, turns each sum into the logit
 // r * sum + bias (written back for the debug copy) and stages the normalised
 // row fp32(x * g * r) (products in double, as rmsnorm_kernel).
+// q8: the staged row holds Q8_K codes per super-block (stage_row_store).
 template <int PL, bool NORM>
 __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, int T, int E, int k,
                                                    int32_t *__restrict__ idx_out, float *__restrict__ w_out, int ks,
                                                    const double *__restrict__ part, const float *__restrict__ x,
                                                    int H, f16 *__restrict__ x_hilo, f16 *__restrict__ x_xs,
                                                    float *__restrict__ x_sinv, const float *__restrict__ norm_w,
-                                                   double eps, const float *__restrict__ bias) {
+                                                   double eps, const float *__restrict__ bias, int q8) {
     __shared__ __attribute__((aligned(16))) double tk_lds[4][64 * PL + kMaxTopK + kMaxTopK / 2];
     __shared__ __attribute__((aligned(16))) double sums[4][64 * PL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -499,10 +500,11 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
         staged_row_normalise(sr, gr, nh, r);
     }
     if (row_in_regs)
-        stage_row_store(sr, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16, x_sinv + (size_t)t * nh);
+        stage_row_store(sr, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16, x_sinv + (size_t)t * nh,
+                        q8 != 0);
     else if (x)
         stage_row_wave(x + (size_t)t * H, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16,
-                       x_sinv + (size_t)t * nh);
+                       x_sinv + (size_t)t * nh, q8 != 0);
 }
 
 // topk_kernel for E > kRankMaxExperts (k rounds of wave argmax; ks = 1): a

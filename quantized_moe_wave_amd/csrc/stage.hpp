@@ -9,7 +9,9 @@
 // the 32-column sums used for the Q4_K min term stay below 2^15 in fp16 too.
 // The kernels multiply the partial products by sinv = 1/s, which is exact.
 // The decode path scales each super-block on its own; the general path
-// (stage_kernel) uses one scale per row. Layout: see common.hpp.
+// (stage_kernel) uses one scale per row. With Q8_K-style activations both
+// stage the codes of each super-block instead (hi = q, lo = 0, 1/s replaced
+// by the block's d). Layout: see common.hpp.
 #pragma once
 #include "common.hpp"
 
@@ -198,11 +200,40 @@ __device__ __forceinline__ void staged_row_normalise(StagedRow &sr, const Staged
     }
 }
 
-// Scale and store a row loaded by stage_row_load.
+// Largest value over the 32 lanes of this lane's half of the wave.
+__device__ __forceinline__ float half_wave_max(float m) {
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    return m;
+}
+
+// Q8_K-style codes of one super-block held as 8 columns per lane by a half
+// wave (q8_code over the block's amax, all in fp32, as stage_row_sb), stored
+// with scale 1 and d = amax / 127 in place of 1/s.
+__device__ __forceinline__ void stage_emit_q8(int b, float4 a, float4 c, int nsb, f16 *__restrict__ hilo_row,
+                                              f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+    float m = fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                    fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+    m = half_wave_max(m);
+    const float is = m > 0.f ? 127.f / m : 0.f;
+    a = float4{q8_code(a.x, is), q8_code(a.y, is), q8_code(a.z, is), q8_code(a.w, is)};
+    c = float4{q8_code(c.x, is), q8_code(c.y, is), q8_code(c.z, is), q8_code(c.w, is)};
+    stage_emit(b, a, c, 1.f, m / 127.f, nsb, hilo_row, xs_row, sinv_row);
+}
+
+// Scale and store a row loaded by stage_row_load (q8: Q8_K codes per
+// super-block instead, stage_emit_q8).
 __device__ __forceinline__ void stage_row_store(const StagedRow &sr, int nsb, f16 *__restrict__ hilo_row,
-                                                f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+                                                f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
+                                                bool q8 = false) {
     const int hb = (threadIdx.x & 63) >> 5;
     const int npairs = (nsb + 1) >> 1;
+    if (q8) {
+#pragma unroll
+        for (int p = 0; p < kStageRegPairs; ++p)
+            if (p < npairs) stage_emit_q8(2 * p + hb, sr.va[p], sr.vb[p], nsb, hilo_row, xs_row, sinv_row);
+        return;
+    }
     float m = 0.f;
 #pragma unroll
     for (int p = 0; p < kStageRegPairs; ++p) {
@@ -219,19 +250,28 @@ __device__ __forceinline__ void stage_row_store(const StagedRow &sr, int nsb, f1
         if (p < npairs) stage_emit(2 * p + hb, sr.va[p], sr.vb[p], sc, sinv, nsb, hilo_row, xs_row, sinv_row);
 }
 
-// Load, scale and store one row (one wave).
+// Load, scale and store one row (one wave; q8: Q8_K codes per super-block).
 __device__ __forceinline__ void stage_row_wave(const float *__restrict__ r, int nsb, f16 *__restrict__ hilo_row,
-                                               f16 *__restrict__ xs_row, float *__restrict__ sinv_row) {
+                                               f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
+                                               bool q8 = false) {
     const int npairs = (nsb + 1) >> 1;
     if (npairs <= kStageRegPairs) {
         StagedRow sr;
         stage_row_load(r, nsb, sr);
-        stage_row_store(sr, nsb, hilo_row, xs_row, sinv_row);
+        stage_row_store(sr, nsb, hilo_row, xs_row, sinv_row, q8);
         return;
     }
     const int lane = threadIdx.x & 63;
     const int f = lane & 31, hb = lane >> 5;
     const int off = (f >> 2) * 32 + (f & 3) * 8;
+    if (q8) {
+        for (int p = 0; p < npairs; ++p) {
+            const int b = 2 * p + hb, bl = min(b, nsb - 1);
+            stage_emit_q8(b, *(const float4 *)(r + bl * kQ4Weights + off),
+                          *(const float4 *)(r + bl * kQ4Weights + off + 4), nsb, hilo_row, xs_row, sinv_row);
+        }
+        return;
+    }
     float m = 0.f;
     for (int c = lane * 4; c < nsb * kQ4Weights; c += 256) {
         const float4 a = *(const float4 *)(r + c);
@@ -246,15 +286,15 @@ __device__ __forceinline__ void stage_row_wave(const float *__restrict__ r, int 
     }
 }
 
-// One wave per row (stage_row_wave).
+// One wave per row (stage_row_wave; q8: Q8_K codes).
 __global__ __launch_bounds__(256) void stage_kernel(const float *__restrict__ src, int rows, int K, int ld_src,
                                                     f16 *__restrict__ hilo, f16 *__restrict__ xs,
-                                                    float *__restrict__ sinv) {
+                                                    float *__restrict__ sinv, int q8) {
     const int nsb = K / kQ4Weights;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     stage_row_wave(src + (size_t)row * ld_src, nsb, hilo + (size_t)row * (2 * K), xs + (size_t)row * nsb * 16,
-                   sinv + (size_t)row * nsb);
+                   sinv + (size_t)row * nsb, q8 != 0);
 }
 
 }  // namespace moe

@@ -69,7 +69,7 @@ def test_block_needs_a_norm_weight():
 
 
 @pytest.mark.parametrize("name,T,mode", [("30b-batch", 64, "block"), ("30b-decode", 2, "block"),
-                                         ("30b-decode", 2, "q8")])
+                                         ("30b-decode", 2, "q8"), ("30b-batch", 64, "q8")])
 def test_graph_replay_matches_eager(name, T, mode):
     """The block (norm launch or fused norm) and the int8-activation variant captured in a HIP graph, replayed
     several times with eager work and synchronisations between replays: every replay equals the eager call,
