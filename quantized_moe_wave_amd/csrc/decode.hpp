@@ -168,16 +168,17 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
 // entries (a pad never beats a real candidate: it is not larger, and on a tie
 // its index is higher). Candidate c's rank counts the keys above its own.
 // Every lane of a wave walks the same range of j, so each LDS read is a
-// broadcast: for E <= 128 candidate c = tid % 128 and waves 0-1 count j < 64,
-// waves 2-3 j >= 64; for larger E candidate c = tid counts all 256. The
-// thread that writes a winner is the one that loaded it (tid == c). lg: 256
-// LDS words of 8 bytes, which hold the keys.
+// broadcast: for E <= 128 candidate c = tid % 128 and the workgroup's first
+// 128 * P threads (P = 2 or 4 parts, as many as it has) count 128 / P keys
+// each, the parts' counts summed by part 0; for larger E candidate c = tid
+// counts all 256. The thread that writes a winner is the one that loaded it
+// (tid == c). lg: 256 LDS words of 8 bytes, which hold the keys.
 __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, double *lg, int *sel_e,
                                            double *sel_v) {
-    __shared__ int rk_hi[128];
+    __shared__ int rk_part[3][128];
     uint64_t *keys = (uint64_t *)lg;
     const int tid = threadIdx.x;
-    const bool act = tid < 256;  // threads past 256 (larger workgroups) only join the barriers
+    const bool act = tid < 256;  // threads past 256 only join the barriers (and count, for E <= 128)
     double v = -INFINITY;
     if (act) {
         const int c = min(tid, E - 1);
@@ -187,9 +188,13 @@ __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, dou
     }
     __syncthreads();
     const bool split = E <= 128;
+    const int nparts = (int)blockDim.x >= 512 ? 4 : 2;  // workgroups of 256 threads or more
+    const int part = split ? tid >> 7 : 0;
+    const bool on = split ? part < nparts : act;
+    const int span = split ? 128 / nparts : 256;
     const int c = split ? (tid & 127) : (tid & 255);
-    const int j0 = split ? ((tid >> 7) & 1) * 64 : 0;
-    const int nj = act ? (split ? 64 : 256) : 0;
+    const int j0 = part * span;
+    const int nj = on ? span : 0;
     const uint64_t key = keys[c];
     int rank = 0;
     for (int jj = 0; jj < nj; jj += 8) {
@@ -203,10 +208,10 @@ __device__ __forceinline__ void topk_block(const double *lrow, int E, int k, dou
 #pragma unroll
         for (int q = 0; q < 8; ++q) rank += (int)(b[q] > key);
     }
-    if (act && split && tid >= 128) rk_hi[c] = rank;
+    if (on && split && part > 0) rk_part[part - 1][c] = rank;
     __syncthreads();
-    if (act && c < E && (!split || tid < 128)) {
-        if (split) rank += rk_hi[c];
+    if (on && c < E && part == 0) {
+        for (int q = 1; q < (split ? nparts : 1); ++q) rank += rk_part[q - 1][c];
         if (rank < k) {
             sel_e[rank] = c;
             sel_v[rank] = v;
@@ -302,6 +307,11 @@ constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS
 //   Q = min-term MFMA of am (k-step sums, hi | lo) with the mins;
 //   acc[i] += sv[i] * (d * P[i] - dmin * Q[i]) with d, dmin of this lane's
 //   weight row (header hdr). afrag(s, hi, lo) supplies A's k-step s.
+// At decode this is a wave's whole share of the work, so its latency is what
+// counts: the hi and lo products go to two accumulators, so that no MFMA
+// waits for the one just before it, and A of k-step s+1 is read (from LDS)
+// while k-step s runs; the two are summed before the scales (two, not four:
+// the gate/up kernel must stay within 80 registers to keep 6 waves per SIMD).
 template <typename AF>
 __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, const u32x4 &hdr, AF afrag, f16x4 am,
                                           const float sv[4], int g, f32x4 &acc) {
@@ -309,9 +319,12 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
     unpack_scales(hdr, sc, mn);
     const float dd = half_bits_to_float(hdr.x & 0xFFFFu);
     const float dmin = half_bits_to_float(hdr.x >> 16);
-    f32x4 P = {0.f, 0.f, 0.f, 0.f};
+    f32x4 Ph = {0.f, 0.f, 0.f, 0.f}, Pl = {0.f, 0.f, 0.f, 0.f};
+    f16x8 ahi[2], alo[2];
+    afrag(0, ahi[0], alo[0]);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+        if (s + 1 < 8) afrag(s + 1, ahi[(s + 1) & 1], alo[(s + 1) & 1]);
         const u32x4 &q = (s < 4) ? q0 : q1;
         const int cc = (s >> 1) & 1;
         const uint32_t dA = cc ? q.z : q.x;
@@ -320,10 +333,8 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
         const f16x2 sc2 = {scv, scv};
         const f16x2 neg2 = sc2 * (f16)(-1024.f);
         const f16x8 B = q_times_scale(dA, dB, s & 1, sc2, neg2);
-        f16x8 ahi, alo;
-        afrag(s, ahi, alo);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, B, P, 0, 0, 0);
-        P = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, B, P, 0, 0, 0);
+        Ph = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi[s & 1], B, Ph, 0, 0, 0);
+        Pl = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo[s & 1], B, Pl, 0, 0, 0);
     }
     f16x4 Bm;
 #pragma unroll
@@ -331,7 +342,9 @@ __device__ __forceinline__ void mma_sb_fn(const u32x4 &q0, const u32x4 &q1, cons
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const f32x4 Q = __builtin_amdgcn_mfma_f32_16x16x16f16(am, Bm, zero, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += sv[i] * (dd * P[i] - dmin * Q[i]);
+    for (int i = 0; i < 4; ++i) {
+        acc[i] += sv[i] * (dd * (Ph[i] + Pl[i]) - dmin * Q[i]);
+    }
 }
 
 // Grid (T*k pairs, I/8 row groups), kGpWaves waves. Pair p = t*k + j: the

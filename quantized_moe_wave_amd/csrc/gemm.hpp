@@ -84,10 +84,17 @@ struct GemmShape {
     static constexpr int BqBuf = Groups * 1024;             // quants of one half super-block
     static constexpr int BLoads = CW;                       // each wave loads its own groups
     static constexpr int HdrBuf = Groups * 256;             // headers of one super-block
-    // k-step sums of 64 rows x 32 B: 8 waves load 4 bytes per lane; 4 waves
-    // load 16 (rows 32*(wave%2) + lane/2; waves 2, 3 repeat waves 0, 1)
-    static constexpr int XsBuf = NW == 8 ? 2048 : 4096;
-    static constexpr int HLoads = HdrBuf / (NW * 1024) + 1;  // headers + the k-step sums
+    // headers move as 16-byte loads where they split evenly over the waves,
+    // else as 4-byte loads (a 16 x 128 tile's 2 KB over 4 waves)
+    static constexpr int HdrLoadB = HdrBuf % (NW * 1024) == 0 ? 16 : 4;
+    static constexpr int HdrLoads = HdrBuf / (NW * 64 * HdrLoadB);  // header loads per lane
+    // k-step sums, 32 B per row: 8 waves, or 4 waves on 16-row tiles, load 4
+    // bytes per lane (rows 8*wave + lane/8: 64 or 32 rows, the rows past the
+    // tile's repeating its last); 4 waves on 64-row tiles load 16 (rows
+    // 32*(wave%2) + lane/2; waves 2, 3 repeat waves 0, 1)
+    static constexpr bool XsNarrow = NW == 8 || RB == 1;
+    static constexpr int XsBuf = NW == 8 ? 2048 : (RB == 1 ? 1024 : 4096);
+    static constexpr int HLoads = HdrLoads + 1;  // headers + the k-step sums
     static constexpr int DxBuf = Q8 ? NW * 256 : 0;          // Q8: 64 rows' scales, one copy per wave
     static constexpr int HxLoads = HLoads + (Q8 ? 1 : 0);    // loads of one HX group
     static constexpr size_t DxOff =
@@ -97,7 +104,7 @@ struct GemmShape {
     // output staging (after the main loop, over the same LDS): M rows of up to
     // 16 * Groups floats, padded by 4 floats against bank conflicts
     static constexpr int OutLd = 16 * Groups + 4;
-    static_assert(ALoads >= 1 && ABuf % (NW * 1024) == 0 && HdrBuf % (NW * 1024) == 0,
+    static_assert(ALoads >= 1 && ABuf % (NW * 1024) == 0 && HdrLoads >= 1 && HdrBuf % (NW * 64 * HdrLoadB) == 0,
                   "buffers must split evenly over the waves");
     static_assert((size_t)M * OutLd * sizeof(float) <= SvOff, "output staging must fit below the 1/s copies");
     static_assert(Lds <= 160 * 1024, "LDS budget");
@@ -161,7 +168,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                                               const float *__restrict__ a_sinv, int e, int r0, int rows, int rg0,
                                               int wave, f32x4 (&X)[RB][CW], float (&fcur)[CW]) {
     using Sh = GemmShape<RB, CW, NW, Q8>;
-    constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHLoads = Sh::HLoads, kHxLoads = Sh::HxLoads;
+    constexpr int kALoads = Sh::ALoads, kBLoads = Sh::BLoads, kHxLoads = Sh::HxLoads;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
     const int K = nsb * kQ4Weights;
@@ -192,18 +199,19 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
         const int f = (wave * kBLoads + i) * 64 + lane;
         boff[i] = (uint32_t)((f >> 6) * nsb * kGroupSbBytes + (f & 63) * 16);
     }
-    // headers: flat 16-byte slot f -> group f/16, row f%16 (after the group's
-    // 2 KB of quants)
-    uint32_t hoff[kHLoads - 1];
+    // headers: flat HdrLoadB-byte slot f -> group f / (256 / HdrLoadB), piece
+    // f % (256 / HdrLoadB) of its 256 bytes (after the group's 2 KB of quants)
+    constexpr int kHdrLoads = Sh::HdrLoads, kHdrB = Sh::HdrLoadB, kHdrPer = 256 / kHdrB;
+    uint32_t hoff[kHdrLoads];
 #pragma unroll
-    for (int i = 0; i < kHLoads - 1; ++i) {
-        const int f = (wave * (kHLoads - 1) + i) * 64 + lane;
-        hoff[i] = (uint32_t)((f >> 4) * nsb * kGroupSbBytes + kGroupQsBytes + (f & 15) * 16);
+    for (int i = 0; i < kHdrLoads; ++i) {
+        const int f = (wave * kHdrLoads + i) * 64 + lane;
+        hoff[i] = (uint32_t)((f / kHdrPer) * nsb * kGroupSbBytes + kGroupQsBytes + (f % kHdrPer) * kHdrB);
     }
-    // k-step sums: NW == 8: row 8*wave + lane/8, 4-byte piece lane%8;
-    // NW == 4: row 32*(wave%2) + lane/2, 16-byte half lane%2
-    const f16 *xs_p = NW == 8 ? a_xs + (size_t)src_row(8 * wave + (lane >> 3)) * nsb * 16 + (lane & 7) * 2
-                              : a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
+    // k-step sums: XsNarrow: row 8*wave + lane/8, 4-byte piece lane%8;
+    // else row 32*(wave%2) + lane/2, 16-byte half lane%2
+    const f16 *xs_p = Sh::XsNarrow ? a_xs + (size_t)src_row(8 * wave + (lane >> 3)) * nsb * 16 + (lane & 7) * 2
+                                   : a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
 
     auto issue_a = [&](int c) {  // chunk c into ring slot c % 4   (kALoads loads)
         const int b = c >> 2, q = c & 3;
@@ -218,11 +226,15 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
         for (int i = 0; i < kBLoads; ++i) load_lds16(wtile + boff[i] + src, dst + i * 1024);
     };
     auto issue_hx = [&](int b) {  // headers + k-step sums (+ Q8 row scales) of super-block b into buffer b % 2   (kHxLoads loads)
-        uint8_t *dst = hbuf + (b & 1) * Sh::HdrBuf + wave * (kHLoads - 1) * 1024;
+        uint8_t *dst = hbuf + (b & 1) * Sh::HdrBuf + wave * kHdrLoads * 64 * kHdrB;
 #pragma unroll
-        for (int i = 0; i < kHLoads - 1; ++i)
-            load_lds16(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 1024);
-        if (NW == 8)
+        for (int i = 0; i < kHdrLoads; ++i) {
+            if (kHdrB == 16)
+                load_lds16(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 1024);
+            else
+                load_lds4(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 256);
+        }
+        if (Sh::XsNarrow)
             load_lds4(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 256);
         else
             load_lds16(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 1024);
@@ -323,7 +335,8 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     // 0x002 VALU, 0x020 global load)
     auto interleave = [&](int nld) {
         constexpr int kM = (Q8 ? 1 : 2) * RB * CW;
-        constexpr int kDs = ((Q8 ? 1 : 2) * RB + CW + 1) / 2;
+        constexpr int kDs0 = ((Q8 ? 1 : 2) * RB + CW + 1) / 2;
+        constexpr int kDs = kDs0 < kM ? kDs0 : kM - 1;  // at least one MFMA left for the VALU groups
         constexpr int kValuPer = (CW * 10 + (kM - kDs) - 1) / (kM - kDs) + 1;
         const int every = nld > 0 ? (kM - kDs) / nld : kM;
 #pragma unroll
@@ -559,15 +572,17 @@ __device__ __forceinline__ TailSplit tail_split(int ntl, int ncb, int x, int C) 
 }
 
 // Waves per SIMD the register budget is sized for: big tiles run one
-// workgroup per CU (NW / 4 waves per SIMD); 16-row tiles two (their LDS allows
-// two workgroups), so they must fit 256 registers (with a budget of 512 the
-// compiler parks values in accumulator registers and moves them back and forth).
-template <int RB, int NW>
-constexpr int gemm_waves_per_simd() { return RB == 1 ? 2 : NW / 4; }
+// workgroup per CU (NW / 4 waves per SIMD); 16-row tiles as many workgroups
+// as their LDS allows (two of 16 x 256; four of 16 x 128, three with the Q8
+// row scales), so they must fit 256 or 128 registers (with a budget of 512
+// the compiler parks values in accumulator registers and moves them back and
+// forth).
+template <int RB, int CW, int NW>
+constexpr int gemm_waves_per_simd() { return RB == 1 ? (CW == 2 ? 4 : 2) : NW / 4; }
 
 template <bool GATEUP, int RB, int CW, int NW, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 1) __attribute__((
-    amdgpu_waves_per_eu(gemm_waves_per_simd<RB, NW>(), gemm_waves_per_simd<RB, NW>()))) void expert_gemm_kernel(
+    amdgpu_waves_per_eu(gemm_waves_per_simd<RB, CW, NW>(), gemm_waves_per_simd<RB, CW, NW>()))) void expert_gemm_kernel(
     const uint8_t *__restrict__ W, int ngroups, int nsb, const int4 *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, const int32_t *__restrict__ entries, int k, const f16 *__restrict__ a_hilo,
     const f16 *__restrict__ a_xs, const float *__restrict__ a_sinv, float *__restrict__ outp, int out_ld, int C,

@@ -392,10 +392,10 @@ hipError_t gemm_lds_limits() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
-        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 4, 4, Q8>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4, Q8>::Lds),
-        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 4, 4, Q8>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 4, 4, Q8>::Lds)};
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 2, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 2, 4, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 2, 4, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 2, 4, Q8>::Lds)};
     for (hipError_t e : a)
         if (e != hipSuccess) return e;
     return hipSuccess;
@@ -411,12 +411,13 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     const int S = T * k;
     const int nh = H / kQ4Weights, ni = I / kQ4Weights;
     // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
-    // (see gemm.hpp); 16-row x 256-column tiles (4 waves) for buckets of at
-    // most 16 entries, 64-row x 512-column tiles (8 waves) for larger ones, or
-    // 64 x 256 (4 waves) where the weight groups do not split into blocks of 32.
+    // (see gemm.hpp); 16-row x 128-column tiles (4 waves, four workgroups per
+    // CU) for buckets of at most 16 entries, 64-row x 512-column tiles (8
+    // waves) for larger ones, or 64 x 256 (4 waves) where the weight groups do
+    // not split into blocks of 32.
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
     const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
-    using Small = GemmShape<1, 4, 4, Q8>;
+    using Small = GemmShape<1, 2, 4, Q8>;
     using Big = GemmShape<4, 4, 8, Q8>;
     using BigN = GemmShape<4, 4, 4, Q8>;
     // big tiles: the 8-wave launch leaves each XCD's split tail units (see
@@ -424,7 +425,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     // only where there are enough pairs for several big tiles per XCD (with
     // few or none the extra launch costs more than it saves)
     const int C = S >= (size_t)E * kGemmMinRows ? h->cus_per_xcd : 0;
-    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 4, 4, Q8>, dim3(8 * (gu_groups / Small::Groups) * ms8),
+    launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 2, 4, Q8>, dim3(8 * (gu_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
                w.x_xs, w.x_sinv, w.h, I, 0, 0);
     if (S >= kGemmMinRows) {
@@ -440,7 +441,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     launch(pf, kStStageH, stage_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), st, w.h, S, I, I, w.h_hilo, w.h_xs,
            w.h_sinv, (int)Q8);
 
-    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 4, 4, Q8>, dim3(8 * (dn_groups / Small::Groups) * ms8),
+    launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 2, 4, Q8>, dim3(8 * (dn_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
                w.h_xs, w.h_sinv, w.Y, H, 0, 0);
     if (S >= kGemmMinRows) {
