@@ -283,10 +283,11 @@ class Bench:
         self.layers = []
 
 
-def profile_record(kernel: str, which: str):
-    """Per-dispatch counter figures of `kernel` committed under profiles/ (which = "traffic": HBM bytes from
-    rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by the plain-copy calibration; "sq": MFMA-busy and VALU figures from SQ
-    counters), or None if not measured or if the kernel's sources changed since (hash of the listed files)."""
+def profile_record(kernel: str, workload: str, which: str):
+    """Per-dispatch counter figures of `kernel` on `workload` committed under profiles/ (which = "traffic": HBM bytes
+    from rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by the plain-copy calibration; "sq": MFMA-busy and VALU figures
+    from SQ counters), or None if not measured on that workload or if the kernel's sources changed since (hash of
+    the listed files). Records are keyed "<kernel> @ <workload>": the figures depend on the routing."""
     import hashlib
     import re
 
@@ -297,7 +298,7 @@ def profile_record(kernel: str, which: str):
     if not m:
         return None
     data = json.loads(m.group(1))
-    k = data["kernels"].get(kernel)
+    k = data["kernels"].get(f"{kernel} @ {workload}")
     if k is None:
         return None
     h = hashlib.sha256()
@@ -350,15 +351,15 @@ def kernel_roofline(b: Bench, steps: int, kind: str) -> dict | None:
         work = sum(s[per] for s in st) * gate_up_bytes_per_expert(wl)
         achieved = work / (total_ms * 1e-3) / 1e9
         rec = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profile_record(pkey, "traffic"),
+               "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profile_record(pkey, wl.name, "traffic"),
                "algorithmic_bytes_per_launch": int(round(work / launches))}
     else:
         work = sum(2.0 * s["rows_big"] * 2 * wl.inter * wl.hidden for s in st)
         achieved = work / (total_ms * 1e-3) / 1e12
         rec = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-               "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": profile_record(pkey, "traffic"),
+               "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": profile_record(pkey, wl.name, "traffic"),
                "algorithmic_flops_per_launch": round(work / launches)}
-        sq = profile_record(pkey, "sq")
+        sq = profile_record(pkey, wl.name, "sq")
         if sq:
             rec.update(sq)
     rec["kernel"] = f"{pkey} ({' + '.join(stages)})"
