@@ -15,8 +15,10 @@
 // (e, first entry, rows, 0), in expert order. n_tiles[0] = number of small
 // tiles, n_tiles[1] = number of GEMM tiles.
 //
-// Two launches over chunks of kBkChunk consecutive pairs (one pair per
-// thread), with integer arithmetic only:
+// Up to kBk1MaxPairs pairs over at most kBk1MaxExperts experts: one launch of
+// one workgroup (bucket_single_kernel, below); otherwise two launches over
+// chunks of kBkChunk consecutive pairs (one pair per thread), with integer
+// arithmetic only:
 //   bucket_hist_kernel     the expert histogram of each chunk -> hist[chunk][E]
 //   bucket_scatter_kernel  each chunk: totals and its prefix over earlier
 //                          chunks from hist, the exclusive scan over experts,
@@ -191,6 +193,133 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
             big_tiles[wcnt[3][e] + i] = make_int4(e, off + i * kGemmM, min(kGemmM, c - i * kGemmM), 0);
         for (int i = 0; i < nsm; ++i)
             tiles[wcnt[2][e] + i] = make_int4(e, off + i * kTileM, min(kTileM, c - i * kTileM), 0);
+    }
+    if (tid == 0) {
+        n_tiles[0] = ns;
+        n_tiles[1] = nb;
+    }
+}
+
+// Single-workgroup bucketing for small calls: the same layout in one launch,
+// for S <= kBk1MaxPairs pairs over E <= kBk1MaxExperts experts (at a few
+// thousand pairs two launches cost more than the work; at tens of thousands
+// one CU's equal-key matching costs more than the second launch). Wave w owns
+// the pairs [w*G*64, (w+1)*G*64), G = ceil(S / (64 * kBk1Waves)) groups of 64
+// (its keys loaded up front). Pass 1 counts each wave's pairs per expert (per
+// group one LDS add per distinct expert, by its lowest lane); the totals'
+// exclusive scan over experts gives each expert's first entry, and within an
+// expert the waves follow in order, so each (wave, expert) count becomes that
+// wave's first entry for the expert. Pass 2 walks the groups again: a pair's
+// entry is its wave's next entry for its expert plus the number of equal keys
+// in lower lanes, and the lowest lane advances the wave's next entry. Then
+// counts, offsets and the tile lists, as bucket_scatter_kernel's chunk 0.
+constexpr int kBk1Waves = 16;
+constexpr int kBk1MaxExperts = 256;
+constexpr int kBk1MaxPairs = 4096;
+constexpr int kBk1MaxGroups = kBk1MaxPairs / (kBk1Waves * 64);  // 64-pair groups per wave
+
+// Exclusive scan of one value per thread over a workgroup of kBk1Waves waves;
+// *total = the sum. Two barriers (red: kBk1Waves ints).
+__device__ __forceinline__ int bk1_scan(int v, int *red, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) red[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kBk1Waves; ++w) {
+        before += w < wave ? red[w] : 0;
+        all += red[w];
+    }
+    *total = all;
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Grid: one workgroup of kBk1Waves * 64 threads; 1 <= S <= kBk1MaxPairs.
+__global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
+    const int32_t *__restrict__ idx, int S, int E, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ entries, int32_t *__restrict__ pos, int4 *__restrict__ tiles, int4 *__restrict__ big_tiles,
+    int32_t *__restrict__ n_tiles) {
+    __shared__ int wh[kBk1Waves][kBk1MaxExperts];  // per (wave, expert): count, then next entry
+    __shared__ int tot[kBk1MaxExperts], off_l[kBk1MaxExperts];
+    __shared__ int red[kBk1Waves];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = (S + kBk1Waves * 64 - 1) / (kBk1Waves * 64);
+    const int s0 = wave * G * 64 + lane;
+    // loads unconditional (index clamped) so that all of them are in flight together
+    uint32_t keys[kBk1MaxGroups];
+#pragma unroll
+    for (int i = 0; i < kBk1MaxGroups; ++i) keys[i] = (uint32_t)idx[min(s0 + i * 64, S - 1)];
+#pragma unroll
+    for (int i = 0; i < kBk1MaxGroups; ++i)
+        if (!(i < G && s0 + i * 64 < S)) keys[i] = (uint32_t)kMaxExperts;
+    for (int i = tid; i < kBk1Waves * kBk1MaxExperts; i += kBk1Waves * 64) (&wh[0][0])[i] = 0;
+    __syncthreads();
+    // pass 1: counts per (wave, expert)
+#pragma unroll
+    for (int i = 0; i < kBk1MaxGroups; ++i) {
+        if (i < G) {
+            const uint32_t key = keys[i];
+            const uint64_t m = lanes_with_key(key);
+            if (key < (uint32_t)E && (m & lanes_below()) == 0) wh[wave][key] += __popcll(m);
+        }
+    }
+    __syncthreads();
+    // totals, their exclusive scan over experts, and each wave's first entry
+    int t_e = 0;
+    if (tid < E)
+        for (int w = 0; w < kBk1Waves; ++w) t_e += wh[w][tid];
+    int n_all;
+    const int first = bk1_scan(t_e, red, &n_all);
+    if (tid < E) {
+        tot[tid] = t_e;
+        off_l[tid] = first;
+        int run = first;
+        for (int w = 0; w < kBk1Waves; ++w) {
+            const int c = wh[w][tid];
+            wh[w][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // pass 2: places, in pair order within each wave
+#pragma unroll
+    for (int i = 0; i < kBk1MaxGroups; ++i) {
+        if (i < G) {
+            const uint32_t key = keys[i];
+            const uint64_t m = lanes_with_key(key);
+            if (key < (uint32_t)E) {
+                const int base = wh[wave][key];
+                const int p = base + __popcll(m & lanes_below());
+                const int s = s0 + i * 64;
+                entries[p] = s;
+                pos[s] = p;
+                if ((m & lanes_below()) == 0) wh[wave][key] = base + __popcll(m);
+            }
+        }
+    }
+    // counts, offsets and the tile lists
+    const int c_e = tid < E ? tot[tid] : 0;
+    if (tid < E) {
+        counts[tid] = c_e;
+        offsets[tid] = off_l[tid];
+    }
+    if (tid == 0) offsets[E] = S;
+    int ns, nb;
+    const int so = bk1_scan(tid < E ? small_tiles_of(c_e) : 0, red, &ns);
+    const int bo = bk1_scan(tid < E ? gemm_tiles_of(c_e) : 0, red, &nb);
+    if (tid < E) {
+        const int o = off_l[tid];
+        for (int i = 0; i < gemm_tiles_of(c_e); ++i)
+            big_tiles[bo + i] = make_int4(tid, o + i * kGemmM, min(kGemmM, c_e - i * kGemmM), 0);
+        for (int i = 0; i < small_tiles_of(c_e); ++i)
+            tiles[so + i] = make_int4(tid, o + i * kTileM, min(kTileM, c_e - i * kTileM), 0);
     }
     if (tid == 0) {
         n_tiles[0] = ns;

@@ -4,7 +4,9 @@
 // forward(T) enqueues, all on the caller's stream, with no host wait:
 //   1. router_kernel   logits (fp64), top-k, renormalised weights (a few
 //                      tokens), or router_logits_kernel + topk_kernel
-//   2. bucket_hist_kernel, bucket_scatter_kernel: stable counting sort of
+//   2. bucket_single_kernel (one workgroup; up to 4096 pairs over at most
+//                      256 experts), else bucket_hist_kernel +
+//                      bucket_scatter_kernel: stable counting sort of
 //                      (token, slot) by expert + tiles
 //   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums
 //   4. expert GATEUP   gate/up Q4_K MFMA + SiLU(g)*u -> h[slot][I]
@@ -537,10 +539,15 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
         }
     }
 
-    const int nchunks = bucket_chunks(S);
-    launch(pf, kStBucket, bucket_hist_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist);
-    launch(pf, kStBucketScatter, bucket_scatter_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist,
-           w.counts, w.offsets, w.entries, w.pos, w.tiles, w.big_tiles, w.n_tiles);
+    if (S <= kBk1MaxPairs && E <= kBk1MaxExperts) {
+        launch(pf, kStBucket, bucket_single_kernel, dim3(1), dim3(kBk1Waves * 64), st, idx, S, E, w.counts, w.offsets,
+               w.entries, w.pos, w.tiles, w.big_tiles, w.n_tiles);
+    } else {
+        const int nchunks = bucket_chunks(S);
+        launch(pf, kStBucket, bucket_hist_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist);
+        launch(pf, kStBucketScatter, bucket_scatter_kernel, dim3(nchunks), dim3(kBkChunk), st, idx, S, E, w.hist,
+               w.counts, w.offsets, w.entries, w.pos, w.tiles, w.big_tiles, w.n_tiles);
+    }
 
     if (!staged_x)
         launch(pf, kStStageX, stage_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), st, x, T, H, H, w.x_hilo,

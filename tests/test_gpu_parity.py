@@ -83,6 +83,16 @@ def test_ragged_token_counts(T):
     parity.check_parity(inp2, g)
 
 
+@pytest.mark.parametrize("T", [2047, 2048, 2049])
+def test_bucketing_paths(T):
+    """Around the switch between the one-workgroup bucketing (up to 4096 pairs) and the two-launch one: the tiny
+    layer (k = 2) at 4094, 4096 and 4098 pairs, buckets of several hundred pairs (64-row tiles)."""
+    print(f"[parity] tiny T={T} ({2 * T} pairs)", flush=True)
+    inp, layer, _ = _layer("tiny", seed=9)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=60 + T))
+    parity.check_parity(inp2, g)
+
+
 def test_one_expert_takes_every_token():
     print("[parity] tiny, expert 0 forced for all tokens", flush=True)
     bias = np.zeros(8, np.float32)
