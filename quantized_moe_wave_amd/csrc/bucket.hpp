@@ -11,7 +11,8 @@
 // below e, offsets[E] = T*k; entries[offsets[e] + r] = t*k + j for the r-th
 // pair in token order that chose e. A bucket of at least kGemmMinRows entries
 // is cut into tiles of up to kGemmM rows for the grouped GEMM (big_tiles);
-// a smaller one into tiles of up to kTileM rows (tiles). Tile records are
+// a smaller one into tiles of up to kTileM rows (tiles); in calls with
+// all_small_tiles (gemm.hpp) every bucket into kTileM-row tiles. Tile records are
 // (e, first entry, rows, 0), in expert order. n_tiles[0] = number of small
 // tiles, n_tiles[1] = number of GEMM tiles.
 //
@@ -35,9 +36,14 @@
 
 namespace moe {
 
-// GEMM tiles and 16-row tiles of a bucket of c entries.
-__device__ __forceinline__ int gemm_tiles_of(int c) { return c >= kGemmMinRows ? (c + kGemmM - 1) / kGemmM : 0; }
-__device__ __forceinline__ int small_tiles_of(int c) { return c >= kGemmMinRows ? 0 : (c + kTileM - 1) / kTileM; }
+// GEMM tiles and 16-row tiles of a bucket of c entries (all: all_small_tiles
+// of the call, every bucket in 16-row tiles).
+__device__ __forceinline__ int gemm_tiles_of(int c, bool all) {
+    return !all && c >= kGemmMinRows ? (c + kGemmM - 1) / kGemmM : 0;
+}
+__device__ __forceinline__ int small_tiles_of(int c, bool all) {
+    return all || c < kGemmMinRows ? (c + kTileM - 1) / kTileM : 0;
+}
 
 constexpr int kBkChunk = 256;  // pairs per chunk = threads per workgroup
 constexpr int kBkLoads = 16;   // histogram entries a thread has in flight
@@ -175,12 +181,13 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
     if (chunk != 0) return;
     // chunk 0: counts, offsets and the tile lists (wcnt is reused once every
     // thread has placed its pair)
+    const bool all = all_small_tiles(S, E);
     __syncthreads();
     for (int e = tid; e < E; e += kBkChunk) {
         counts[e] = tot[e];
         offsets[e] = off_l[e];
-        wcnt[0][e] = small_tiles_of(tot[e]);
-        wcnt[1][e] = gemm_tiles_of(tot[e]);
+        wcnt[0][e] = small_tiles_of(tot[e], all);
+        wcnt[1][e] = gemm_tiles_of(tot[e], all);
     }
     if (tid == 0) offsets[E] = S;
     __syncthreads();
@@ -188,7 +195,7 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
     const int nb = block_scan_lds(wcnt[1], wcnt[3], E, red);
     for (int e = tid; e < E; e += kBkChunk) {
         const int c = tot[e], off = off_l[e];
-        const int nsm = small_tiles_of(c), nbg = gemm_tiles_of(c);
+        const int nsm = small_tiles_of(c, all), nbg = gemm_tiles_of(c, all);
         for (int i = 0; i < nbg; ++i)
             big_tiles[wcnt[3][e] + i] = make_int4(e, off + i * kGemmM, min(kGemmM, c - i * kGemmM), 0);
         for (int i = 0; i < nsm; ++i)
@@ -312,13 +319,14 @@ __global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
     }
     if (tid == 0) offsets[E] = S;
     int ns, nb;
-    const int so = bk1_scan(tid < E ? small_tiles_of(c_e) : 0, red, &ns);
-    const int bo = bk1_scan(tid < E ? gemm_tiles_of(c_e) : 0, red, &nb);
+    const bool all = all_small_tiles(S, E);
+    const int so = bk1_scan(tid < E ? small_tiles_of(c_e, all) : 0, red, &ns);
+    const int bo = bk1_scan(tid < E ? gemm_tiles_of(c_e, all) : 0, red, &nb);
     if (tid < E) {
         const int o = off_l[tid];
-        for (int i = 0; i < gemm_tiles_of(c_e); ++i)
+        for (int i = 0; i < gemm_tiles_of(c_e, all); ++i)
             big_tiles[bo + i] = make_int4(tid, o + i * kGemmM, min(kGemmM, c_e - i * kGemmM), 0);
-        for (int i = 0; i < small_tiles_of(c_e); ++i)
+        for (int i = 0; i < small_tiles_of(c_e, all); ++i)
             tiles[so + i] = make_int4(tid, o + i * kTileM, min(kTileM, c_e - i * kTileM), 0);
     }
     if (tid == 0) {

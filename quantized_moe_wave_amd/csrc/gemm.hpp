@@ -122,8 +122,17 @@ __host__ __device__ inline int max_gemm_tiles(int S, int E) {
     const int big_buckets = S / kGemmMinRows < E ? S / kGemmMinRows : E;
     return S / kGemmM + big_buckets;
 }
-// Upper bound on 16-row tiles: one per bucket of fewer than kGemmMinRows entries.
-__host__ __device__ inline int max_small_tiles(int S, int E) { return S < E ? S : E; }
+// Calls whose buckets average at most kTileM pairs (S <= E * kTileM) cut every
+// bucket into 16-row tiles and launch no 64-row GEMM: there the 64-row launches
+// would mostly find no tile, and a rare larger bucket costs a few more passes
+// over its expert's weights.
+__host__ __device__ inline bool all_small_tiles(int S, int E) { return S <= E * kTileM; }
+// Upper bound on 16-row tiles: one per bucket of fewer than kGemmMinRows
+// entries, or with all_small_tiles ceil(c / kTileM) <= c / kTileM + 1 per bucket.
+__host__ __device__ inline int max_small_tiles(int S, int E) {
+    const int buckets = S < E ? S : E;
+    return all_small_tiles(S, E) ? S / kTileM + buckets : buckets;
+}
 
 __device__ __forceinline__ void load_lds16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);

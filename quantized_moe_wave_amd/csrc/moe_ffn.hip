@@ -95,9 +95,13 @@ struct Workspace {
     float *dw = nullptr;          // [S] decode path: its renormalised router weight
 };
 
-// 16-row tiles: only buckets of fewer than kGemmMinRows (<= 16) entries take
-// them, one tile each.
-int max_tiles(int S, int E) { return max_small_tiles(S, E); }
+// 16-row tiles: buckets of fewer than kGemmMinRows (<= 16) entries, one tile
+// each, or in calls with all_small_tiles every bucket. Room for the 16-row tile list of any call of up to S pairs: max_small_tiles
+// over S' <= S (calls with all_small_tiles take up to S'/kTileM + E tiles).
+int max_tiles(int S, int E) {
+    const int s16 = S < E * kTileM ? S : E * kTileM;
+    return s16 / kTileM + (S < E ? S : E);
+}
 static_assert(kGemmMinRows <= kTileM + 1, "a small bucket must fit one 16-row tile");
 
 enum Stage {
@@ -430,7 +434,8 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     launch_lds(pf, kStGateUp, expert_gemm_kernel<true, 1, 2, 4, Q8>, dim3(8 * (gu_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->gu, gu_groups, nh, w.tiles, w.n_tiles, w.entries, k, w.x_hilo,
                w.x_xs, w.x_sinv, w.h, I, 0, 0);
-    if (S >= kGemmMinRows) {
+    const bool big = S >= kGemmMinRows && !all_small_tiles(S, E);  // else no 64-row tile exists
+    if (big) {
         launch_lds(pf, kStGateUpBig, expert_gemm_kernel<true, 4, 4, 8, Q8>, dim3(8 * (gu_groups / Big::Groups) * mg8),
                    dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
                    w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
@@ -446,7 +451,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     launch_lds(pf, kStDown, expert_gemm_kernel<false, 1, 2, 4, Q8>, dim3(8 * (dn_groups / Small::Groups) * ms8),
                dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
                w.h_xs, w.h_sinv, w.Y, H, 0, 0);
-    if (S >= kGemmMinRows) {
+    if (big) {
         if (gemm_big_waves(dn_groups) == 8) {
             launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8, Q8>,
                        dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,

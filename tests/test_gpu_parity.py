@@ -258,6 +258,20 @@ def test_experts_up_to_256(E, T):
     layer.close()
 
 
+@pytest.mark.parametrize("T", [64, 200, 256, 257])
+def test_large_bucket_in_small_call(T):
+    """Calls whose buckets average at most 16 pairs (T*k <= 16*E: T <= 256 here) cut every bucket into 16-row
+    tiles and launch no 64-row GEMM; a bias that sends every token to expert 0 makes one bucket of T pairs there
+    (4, 13 and 16 tiles of 16 rows), and at T = 257 the call takes 64-row tiles again."""
+    print(f"[parity] 30b shape, expert 0 forced, T={T}", flush=True)
+    bias = np.zeros(128, np.float32)
+    bias[0] = 40.0
+    inp, layer, _ = _layer("30b-batch", seed=8, bias=bias)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=88 + T))
+    assert g.counts[0] == T
+    parity.check_parity(inp2, g)
+
+
 @pytest.mark.parametrize("name,T", [("tiny", 300), ("30b-batch", 300)])
 def test_big_tiles_full_parity(name, T):
     """A bias that sends every token to expert 0 makes 128-row grouped-GEMM
