@@ -511,8 +511,10 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
     } else if (T <= 4) {
         launch_router<4, 1>(h, w, pf, T, x, idx, wt, st);
     } else {
-        // few token tiles: split H over more workgroups (partials summed in
-        // split order by the top-k kernel); ks*T*E stays below kRlPartDoubles
+        // few token tiles: split H over more workgroups, up to 256 of them
+        // (partials summed in split order by the top-k kernel; rtiles * ks <=
+        // 256 keeps ks*T*E <= 1024 * rtiles * ks <= kRlPartDoubles; 235b
+        // shape at T = 512: 26.8 -> 16.4 us against a split up to 128)
         // many token tiles: 8 waves per workgroup (two per SIMD) where each
         // wave's share of H is whole 64-column groups; few: 4 waves, and the
         // split over workgroups below supplies the parallelism
@@ -520,7 +522,9 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
         const int nwv = H % 512 == 0 && rtiles >= 128 ? 8 : 4;
         int ks = 1;
         if (E <= kRankMaxExperts)
-            while (ks < kRlMaxSplit && rtiles * ks < 128 && (H / (64 * nwv)) % (2 * ks) == 0) ks *= 2;
+            while (ks < kRlMaxSplit && rtiles * 2 * ks <= 256 && (H / (64 * nwv)) % (2 * ks) == 0) ks *= 2;
+        if (ks > 1 && (size_t)ks * T * E > (size_t)kRlPartDoubles)  // ks = 1 writes the logits directly
+            return fail(MOE_ERR_INVALID_ARG, "internal: router split %d exceeds the partial-logit buffer", ks);
         const dim3 rgrid((T + kRlTok - 1) / kRlTok, (E + kRlExp - 1) / kRlExp, ks);
         // with the block's norm folded in, the router leaves 1/rms and the
         // bias to the top-k launch
