@@ -536,12 +536,21 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
             launch(pf, kStRouter, norm_w ? router_logits_kernel<4, true> : router_logits_kernel<4, false>, rgrid,
                    dim3(256), st, x, h->rw, rbias, T, H, E, w.logits, ks, w.lpart, norm_w);
         if (E <= kRankMaxExperts) {
-            // the top-k launch also stages x (normalised, with the block's norm)
-            auto topk = norm_w ? (E <= 64 ? topk_kernel<1, true> : E <= 128 ? topk_kernel<2, true> : topk_kernel<4, true>)
-                               : (E <= 64 ? topk_kernel<1, false> : E <= 128 ? topk_kernel<2, false>
-                                                                              : topk_kernel<4, false>);
-            launch(pf, kStTopk, topk, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks, w.lpart, x, H,
-                   w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, norm_w ? h->rb : nullptr, q8);
+            // the top-k launch also stages x (normalised, with the block's
+            // norm): one token per workgroup of 4 waves where the row fits
+            // their registers, else one per wave
+            const bool per_token = (nh + 1) / 2 <= kStageRegPairs;
+            auto topk = per_token
+                            ? (norm_w ? (E <= 64 ? topk_token_kernel<1, true> : E <= 128 ? topk_token_kernel<2, true>
+                                                                                         : topk_token_kernel<4, true>)
+                                      : (E <= 64 ? topk_token_kernel<1, false> : E <= 128 ? topk_token_kernel<2, false>
+                                                                                          : topk_token_kernel<4, false>))
+                            : (norm_w ? (E <= 64 ? topk_kernel<1, true> : E <= 128 ? topk_kernel<2, true>
+                                                                                   : topk_kernel<4, true>)
+                                      : (E <= 64 ? topk_kernel<1, false> : E <= 128 ? topk_kernel<2, false>
+                                                                                    : topk_kernel<4, false>));
+            launch(pf, kStTopk, topk, dim3(per_token ? T : (T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt, ks,
+                   w.lpart, x, H, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, norm_w ? h->rb : nullptr, q8);
             staged_x = true;
         } else {
             launch(pf, kStTopk, topk_wide_kernel, dim3((T + 3) / 4), dim3(256), st, w.logits, T, E, k, idx, wt);

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
     __shared__ __attribute__((aligned(16))) double tk_lds[4][64 * PL + kMaxTopK + kMaxTopK / 2];
     __shared__ __attribute__((aligned(16))) double sums[4][64 * PL];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * (blockDim.x >> 6) + wave;  // one token per wave, 1-4 waves per workgroup
     if (t >= T) return;
     const int nh = H / kQ4Weights;
     const bool row_in_regs = x && (nh + 1) / 2 <= kStageRegPairs;
@@ -505,6 +505,123 @@ __global__ __launch_bounds__(256) void topk_kernel(double *__restrict__ logits, 
     else if (x)
         stage_row_wave(x + (size_t)t * H, nh, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16,
                        x_sinv + (size_t)t * nh, q8 != 0);
+}
+
+// topk_kernel with one token per workgroup of 4 waves, for rows that fit the
+// registers ((H / 256 + 1) / 2 <= kStageRegPairs, x non-null): the same
+// results, with the token's chain of dependent steps split four ways. Thread
+// c sums expert c's ks partials (z order); the four waves rank the
+// candidates together (thread (part, c) counts the keys of part's share of
+// the experts above c's, the counts added in LDS); wave w holds and stages
+// the row's super-block pairs w, w + 4, ... (the row's scale from the four
+// waves' maxima). NORM: 1/rms from the sum of squares of the held parts
+// (each square exact in double).
+template <int PL, bool NORM>
+__global__ __launch_bounds__(256) void topk_token_kernel(double *__restrict__ logits, int T, int E, int k,
+                                                         int32_t *__restrict__ idx_out, float *__restrict__ w_out,
+                                                         int ks, const double *__restrict__ part,
+                                                         const float *__restrict__ x, int H, f16 *__restrict__ x_hilo,
+                                                         f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
+                                                         const float *__restrict__ norm_w, double eps,
+                                                         const float *__restrict__ bias, int q8) {
+    constexpr int EP = 64 * PL;       // candidates, padded
+    constexpr int NPART = 256 / EP;   // rank parts (4, 2 or 1)
+    constexpr int SPAN = EP / NPART;  // keys counted per thread
+    static_assert(SPAN % 16 == 0, "16 keys per step");
+    __shared__ __attribute__((aligned(16))) uint64_t keys[EP];
+    __shared__ int rk[NPART][EP];
+    __shared__ double sel_v[kMaxTopK];
+    __shared__ int sel_e[kMaxTopK];
+    __shared__ double red_d[4];
+    __shared__ float red_f[4];
+    const int t = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (t >= T) return;
+    const int nh = H / kQ4Weights;
+    const float *xrow = x + (size_t)t * H;
+    StagedPart sp;
+    stage_pairs_load(xrow, nh, wave, 4, sp);
+
+    // expert tid's logit: partials issued first, the row's 1/rms meanwhile
+    const int c = tid;
+    double pv[kRlMaxSplit];
+    if (ks > 1) {
+#pragma unroll
+        for (int z = 0; z < kRlMaxSplit; ++z) pv[z] = part[((size_t)min(z, ks - 1) * T + t) * E + min(c, E - 1)];
+    } else {
+        pv[0] = logits[(size_t)t * E + min(c, E - 1)];
+    }
+    double r = 1.0;
+    if (NORM) {
+        const double ss = wave_sum(staged_pairs_sumsq(sp, nh));
+        if (lane == 0) red_d[wave] = ss;
+        __syncthreads();
+        r = 1.0 / sqrt((red_d[0] + red_d[1] + red_d[2] + red_d[3]) / (double)H + eps);
+    }
+    double v = pv[0];
+    if (ks > 1) {
+#pragma unroll
+        for (int z = 1; z < kRlMaxSplit; ++z)
+            if (z < ks) v += pv[z];
+    }
+    if (NORM) v = r * v + (bias ? (double)bias[min(c, E - 1)] : 0.0);
+    if (c < E && (ks > 1 || NORM)) logits[(size_t)t * E + c] = v;
+    v = (c < E && v == v) ? v : -INFINITY;  // NaN never wins; entries >= E pad with -inf
+    if (c < EP) keys[c] = rank_key(v, c);
+    __syncthreads();
+
+    // ranks: thread (prt, cand) counts the keys of [prt * SPAN, (prt + 1) * SPAN)
+    // above cand's (prt is uniform per wave, so the key reads broadcast)
+    const int prt = tid / EP, cand = tid % EP;
+    const uint64_t key = keys[cand];
+    int rank = 0;
+#pragma unroll 2
+    for (int j0 = prt * SPAN; j0 < (prt + 1) * SPAN; j0 += 16) {
+        uint64_t a[16];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const ulonglong2 p2 = *(const ulonglong2 *)&keys[j0 + 2 * q];
+            a[2 * q] = p2.x;
+            a[2 * q + 1] = p2.y;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) rank += (int)(a[q] > key);
+    }
+    rk[prt][cand] = rank;
+    __syncthreads();
+    if (c < E) {  // prt == 0 here: cand == c, v is c's
+        int rs = 0;
+#pragma unroll
+        for (int q = 0; q < NPART; ++q) rs += rk[q][c];
+        if (rs < k) {
+            sel_v[rs] = v;
+            sel_e[rs] = c;
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const double ex = (lane < k) ? exp(sel_v[lane] - sel_v[0]) : 0.0;
+        const double z = wave_sum(ex);
+        if (lane < k) {
+            idx_out[(size_t)t * k + lane] = sel_e[lane];
+            w_out[(size_t)t * k + lane] = (float)(ex / z);
+        }
+    }
+
+    // the row: normalised (NORM), scaled by the row's power of two, stored
+    if (NORM) {
+        StagedPart gp;
+        stage_pairs_load(norm_w, nh, wave, 4, gp);
+        staged_pairs_normalise(sp, gp, nh, r);
+    }
+    int se = 0;
+    if (!q8) {
+        const float m = wave_max(staged_pairs_absmax(sp, nh));
+        if (lane == 0) red_f[wave] = m;
+        __syncthreads();
+        se = stage_exponent(fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3])));
+    }
+    staged_pairs_emit(sp, nh, se, x_hilo + (size_t)t * (2 * H), x_xs + (size_t)t * nh * 16, x_sinv + (size_t)t * nh,
+                      q8 != 0);
 }
 
 // topk_kernel for E > kRankMaxExperts (k rounds of wave argmax; ks = 1): a

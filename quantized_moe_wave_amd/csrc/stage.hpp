@@ -118,27 +118,46 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
 // once (every load issued before the first use); longer rows are read twice.
 constexpr int kStageRegPairs = 8;
 
-// A row of at most 2 * kStageRegPairs super-blocks in registers: pair p holds
-// super-block 2p (lanes 0-31) and 2p + 1 (lanes 32-63), 8 columns per lane.
-struct StagedRow {
-    float4 va[kStageRegPairs], vb[kStageRegPairs];
+// Pairs of super-blocks of a row in registers: slot i holds pair p = p0 +
+// ps * i (super-block 2p on lanes 0-31 and 2p + 1 on lanes 32-63, 8 columns
+// per lane). A whole row (p0 = 0, ps = 1) takes up to kStageRegPairs pairs;
+// a workgroup of 4 waves splits a row as p0 = wave, ps = 4.
+template <int SLOTS>
+struct StagedPairs {
+    float4 va[SLOTS], vb[SLOTS];
+    int p0, ps;
 };
+using StagedRow = StagedPairs<kStageRegPairs>;
+constexpr int kStagePartSlots = kStageRegPairs / 4;  // one wave's slots when 4 waves share a row
+using StagedPart = StagedPairs<kStagePartSlots>;
 
-// Issue the loads of a row into sr (no wait: the caller may do other work
-// while they are in flight). Requires (nsb + 1) / 2 <= kStageRegPairs.
-__device__ __forceinline__ void stage_row_load(const float *__restrict__ r, int nsb, StagedRow &sr) {
+// Issue the loads of pairs p0, p0 + ps, ... of a row into sp (no wait: the
+// caller may do other work while they are in flight). Requires the row's
+// (nsb + 1) / 2 pairs to fit: p0 + ps * SLOTS >= (nsb + 1) / 2.
+template <int SLOTS>
+__device__ __forceinline__ void stage_pairs_load(const float *__restrict__ r, int nsb, int p0, int ps,
+                                                 StagedPairs<SLOTS> &sp) {
     const int lane = threadIdx.x & 63;
     const int f = lane & 31, hb = lane >> 5;
     const int off = (f >> 2) * 32 + (f & 3) * 8;
     const int npairs = (nsb + 1) >> 1;
+    sp.p0 = p0;
+    sp.ps = ps;
 #pragma unroll
-    for (int p = 0; p < kStageRegPairs; ++p) {
+    for (int i = 0; i < SLOTS; ++i) {
+        const int p = p0 + ps * i;
         if (p < npairs) {
             const int b = min(2 * p + hb, nsb - 1);  // an odd tail repeats the last block (not stored)
-            sr.va[p] = *(const float4 *)(r + b * kQ4Weights + off);
-            sr.vb[p] = *(const float4 *)(r + b * kQ4Weights + off + 4);
+            sp.va[i] = *(const float4 *)(r + b * kQ4Weights + off);
+            sp.vb[i] = *(const float4 *)(r + b * kQ4Weights + off + 4);
         }
     }
+}
+
+// A whole row (stage_pairs_load with p0 = 0, ps = 1). Requires
+// (nsb + 1) / 2 <= kStageRegPairs.
+__device__ __forceinline__ void stage_row_load(const float *__restrict__ r, int nsb, StagedRow &sr) {
+    stage_pairs_load(r, nsb, 0, 1, sr);
 }
 
 // The 8 columns (a, c) of super-block b owned by this lane, scaled by sc:
@@ -177,10 +196,12 @@ __device__ __forceinline__ void stage_emit(int b, float4 a, float4 c, float sc, 
     }
 }
 
-// The block's RMSNorm on a row loaded by stage_row_load, with its weight gr
+// The block's RMSNorm on pairs loaded by stage_pairs_load, with its weight gp
 // (loaded the same way) and 1/rms r: each value becomes fp32(x * g * r), the
 // products in double.
-__device__ __forceinline__ void staged_row_normalise(StagedRow &sr, const StagedRow &gr, int nsb, double r) {
+template <int SLOTS>
+__device__ __forceinline__ void staged_pairs_normalise(StagedPairs<SLOTS> &sp, const StagedPairs<SLOTS> &gp, int nsb,
+                                                       double r) {
     const int npairs = (nsb + 1) >> 1;
     auto nz = [&](float4 &v, const float4 &g) {
         v.x = (float)((double)v.x * g.x * r);
@@ -191,13 +212,36 @@ __device__ __forceinline__ void staged_row_normalise(StagedRow &sr, const Staged
     // pair by pair (a scheduling fence between pairs), so that the double
     // intermediates of one pair only are live at a time
 #pragma unroll
-    for (int p = 0; p < kStageRegPairs; ++p) {
-        if (p < npairs) {
-            nz(sr.va[p], gr.va[p]);
-            nz(sr.vb[p], gr.vb[p]);
+    for (int i = 0; i < SLOTS; ++i) {
+        if (sp.p0 + sp.ps * i < npairs) {
+            nz(sp.va[i], gp.va[i]);
+            nz(sp.vb[i], gp.vb[i]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+__device__ __forceinline__ void staged_row_normalise(StagedRow &sr, const StagedRow &gr, int nsb, double r) {
+    staged_pairs_normalise(sr, gr, nsb, r);
+}
+
+// This lane's sum of squares (each square exact in double) over the values
+// it holds, the repeated block of an odd tail left out.
+template <int SLOTS>
+__device__ __forceinline__ double staged_pairs_sumsq(const StagedPairs<SLOTS> &sp, int nsb) {
+    const int hb = (threadIdx.x & 63) >> 5;
+    const int npairs = (nsb + 1) >> 1;
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+        const int p = sp.p0 + sp.ps * i;
+        if (p < npairs && 2 * p + hb < nsb) {
+            const float v[8] = {sp.va[i].x, sp.va[i].y, sp.va[i].z, sp.va[i].w,
+                                sp.vb[i].x, sp.vb[i].y, sp.vb[i].z, sp.vb[i].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += (double)v[e] * v[e];
+        }
+    }
+    return ss;
 }
 
 // Largest value over the 32 lanes of this lane's half of the wave.
@@ -221,33 +265,51 @@ __device__ __forceinline__ void stage_emit_q8(int b, float4 a, float4 c, int nsb
     stage_emit(b, a, c, 1.f, m / 127.f, nsb, hilo_row, xs_row, sinv_row);
 }
 
+// This lane's largest magnitude over the values it holds (the repeated block
+// of an odd tail may count: it repeats a value of the row).
+template <int SLOTS>
+__device__ __forceinline__ float staged_pairs_absmax(const StagedPairs<SLOTS> &sp, int nsb) {
+    const int npairs = (nsb + 1) >> 1;
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+        if (sp.p0 + sp.ps * i < npairs) {
+            const float4 a = sp.va[i], c = sp.vb[i];
+            m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
+                               fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)))));
+        }
+    }
+    return m;
+}
+
+// Store the held pairs with the row's scale 2^se (q8: Q8_K codes per
+// super-block instead, stage_emit_q8, and se unused).
+template <int SLOTS>
+__device__ __forceinline__ void staged_pairs_emit(const StagedPairs<SLOTS> &sp, int nsb, int se,
+                                                  f16 *__restrict__ hilo_row, f16 *__restrict__ xs_row,
+                                                  float *__restrict__ sinv_row, bool q8) {
+    const int hb = (threadIdx.x & 63) >> 5;
+    const int npairs = (nsb + 1) >> 1;
+    const float sc = ldexpf(1.f, se), sinv = ldexpf(1.f, -se);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+        const int p = sp.p0 + sp.ps * i;
+        if (p < npairs) {
+            if (q8)
+                stage_emit_q8(2 * p + hb, sp.va[i], sp.vb[i], nsb, hilo_row, xs_row, sinv_row);
+            else
+                stage_emit(2 * p + hb, sp.va[i], sp.vb[i], sc, sinv, nsb, hilo_row, xs_row, sinv_row);
+        }
+    }
+}
+
 // Scale and store a row loaded by stage_row_load (q8: Q8_K codes per
 // super-block instead, stage_emit_q8).
 __device__ __forceinline__ void stage_row_store(const StagedRow &sr, int nsb, f16 *__restrict__ hilo_row,
                                                 f16 *__restrict__ xs_row, float *__restrict__ sinv_row,
                                                 bool q8 = false) {
-    const int hb = (threadIdx.x & 63) >> 5;
-    const int npairs = (nsb + 1) >> 1;
-    if (q8) {
-#pragma unroll
-        for (int p = 0; p < kStageRegPairs; ++p)
-            if (p < npairs) stage_emit_q8(2 * p + hb, sr.va[p], sr.vb[p], nsb, hilo_row, xs_row, sinv_row);
-        return;
-    }
-    float m = 0.f;
-#pragma unroll
-    for (int p = 0; p < kStageRegPairs; ++p) {
-        if (p < npairs) {
-            const float4 a = sr.va[p], c = sr.vb[p];
-            m = fmaxf(m, fmaxf(fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))),
-                               fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w)))));
-        }
-    }
-    const int se = stage_exponent(wave_max(m));
-    const float sc = ldexpf(1.f, se), sinv = ldexpf(1.f, -se);
-#pragma unroll
-    for (int p = 0; p < kStageRegPairs; ++p)
-        if (p < npairs) stage_emit(2 * p + hb, sr.va[p], sr.vb[p], sc, sinv, nsb, hilo_row, xs_row, sinv_row);
+    const int se = q8 ? 0 : stage_exponent(wave_max(staged_pairs_absmax(sr, nsb)));
+    staged_pairs_emit(sr, nsb, se, hilo_row, xs_row, sinv_row, q8);
 }
 
 // Load, scale and store one row (one wave; q8: Q8_K codes per super-block).
