@@ -285,3 +285,31 @@ def test_big_tiles_full_parity(name, T):
     inp2, g = _run(inp, layer, _x(inp, T, seed=77))
     assert g.counts[0] == T
     parity.check_parity(inp2, g)
+
+
+@pytest.mark.parametrize("H,T", [(1280, 37), (1536, 40), (4352, 21)])
+def test_row_lengths(H, T):
+    """Hidden sizes around the top-k launch's split of a row over four waves: 5 super-blocks (an odd tail, and the
+    fourth wave holds no pair), 6 (the router split over H, partials added by the top-k launch) and 17 (longer than
+    the four waves' registers hold: one wave per token, the row read twice); the layer, and the block with its
+    norm (folded into the top-k launch, or a launch of its own for the 17-block row)."""
+    import dataclasses
+
+    import torch
+
+    import oracle
+
+    print(f"[parity] H={H} T={T}", flush=True)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name=f"h{H}", hidden=H)
+    inp = synth.make_inputs(wl, seed=60 + H // 256)
+    layer, dev = parity.make_layer(inp)
+    inp2, g = _run(inp, layer, _x(inp, T, seed=70 + T))
+    parity.check_parity(inp2, g)
+    hidden = (synth.gen_x(3, 11, T, H) * np.float32(3.0)).astype(np.float32)
+    gn = synth.gen_norm(3, 0, H)
+    layer.set_norm(torch.from_numpy(gn), synth.NORM_EPS)
+    run = parity.run_gpu(layer, torch.from_numpy(hidden).cuda(), block=True)
+    layer.close()
+    xn = oracle.rms_norm(hidden, gn, synth.NORM_EPS).astype(np.float32)
+    inp_n = synth.LayerInputs(wl.with_tokens(T), xn, inp.router, inp.bias, inp.gate, inp.up, inp.down)
+    parity.check_parity(inp_n, run, resid=hidden)
