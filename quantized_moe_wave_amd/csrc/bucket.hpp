@@ -46,11 +46,12 @@ __device__ __forceinline__ int small_tiles_of(int c, bool all) {
 }
 
 constexpr int kBkChunk = 256;  // pairs per chunk = threads per workgroup
-constexpr int kBkLoads = 16;   // histogram entries a thread has in flight
-constexpr int kBkKeyBits = 11; // keys 0..kMaxExperts (kMaxExperts: "no pair")
-static_assert(kMaxExperts < (1 << kBkKeyBits), "keys must fit the ballot match");
+constexpr int kBkLoads = 32;   // histogram entries a thread has in flight (64 chunks in one round)
 
 __host__ __device__ inline int bucket_chunks(int S) { return (S + kBkChunk - 1) / kBkChunk; }
+
+constexpr int kBkKeyBits = 11; // keys 0..kMaxExperts (kMaxExperts: "no pair")
+static_assert(kMaxExperts < (1 << kBkKeyBits), "keys must fit the ballot match");
 
 // Lanes of this wave whose key equals this lane's (every lane must call it).
 __device__ __forceinline__ uint64_t lanes_with_key(uint32_t key) {
@@ -72,28 +73,31 @@ __device__ __forceinline__ uint64_t lanes_below() {
 // Exclusive scan over n <= 4 * 256 values v[0..n) in LDS by a 256-thread
 // workgroup (thread t owns v[t*per .. t*per + per), per = ceil(n / 256)):
 // out[i] = sum of v below i (out may alias v); returns the total. Two barriers.
-__device__ __forceinline__ int block_scan_lds(const int *v, int *out, int n, int *red) {
+// V = long long scans two 32-bit counts packed in one value (no carry out of
+// the low half: its total stays below 2^32).
+template <typename V>
+__device__ __forceinline__ V block_scan_lds(const V *v, V *out, int n, V *red) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int per = (n + 255) / 256;
-    int loc[4] = {0, 0, 0, 0};
-    int sum = 0;
+    V loc[4] = {0, 0, 0, 0};
+    V sum = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = tid * per + i;
         if (i < per && j < n) loc[i] = v[j];
         sum += loc[i];
     }
-    int incl = sum;
+    V incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, kWave);
+        const V y = __shfl_up(incl, o, kWave);
         if (lane >= o) incl += y;
     }
     if (lane == 63) red[wave] = incl;
     __syncthreads();
-    int run = incl - sum;
+    V run = incl - sum;
     for (int w = 0; w < wave; ++w) run += red[w];
-    const int total = red[0] + red[1] + red[2] + red[3];
+    const V total = red[0] + red[1] + red[2] + red[3];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int j = tid * per + i;
@@ -149,16 +153,16 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
         for (int e = tid % E; e < E; e += kBkChunk) {
             int sum_t = 0, sum_p = 0;
             for (int c0 = tid / E * (E <= kBkChunk); c0 < nchunks; c0 += tpe * kBkLoads) {
+                // loads unconditional (chunk clamped), so that no branch splits
+                // them and all are in flight together
                 int v[kBkLoads];
+#pragma unroll
+                for (int i = 0; i < kBkLoads; ++i) v[i] = hist[(size_t)min(c0 + i * tpe, nchunks - 1) * E + e];
 #pragma unroll
                 for (int i = 0; i < kBkLoads; ++i) {
                     const int c = c0 + i * tpe;
-                    v[i] = c < nchunks ? hist[(size_t)c * E + e] : 0;
-                }
-#pragma unroll
-                for (int i = 0; i < kBkLoads; ++i) {
-                    sum_t += v[i];
-                    sum_p += c0 + i * tpe < chunk ? v[i] : 0;
+                    sum_t += c < nchunks ? v[i] : 0;
+                    sum_p += c < chunk ? v[i] : 0;
                 }
             }
             atomicAdd(&tot[e], sum_t);
@@ -168,9 +172,23 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
     const uint64_t m = lanes_with_key(key);
     if (key < (uint32_t)E && (m & lanes_below()) == 0) wcnt[wave][key] = __popcll(m);
     __syncthreads();
-    // first entry of every expert: exclusive scan of the totals
+    // first entry of every expert: exclusive scan of the totals; chunk 0 also
+    // scans the tile counts here, so that no barrier follows a global store
+    // (each would wait for the stores to complete)
     __shared__ int off_l[kMaxExperts];
+    __shared__ long long toff[kMaxExperts];  // chunk 0: first 16-row tile (low half), first 64-row tile (high)
+    __shared__ long long red2[4];
     block_scan_lds(tot, off_l, E, red);
+    const bool all = all_small_tiles(S, E);
+    int ns = 0, nb = 0;
+    if (chunk == 0) {
+        for (int e = tid; e < E; e += kBkChunk)
+            toff[e] = (long long)small_tiles_of(tot[e], all) + ((long long)gemm_tiles_of(tot[e], all) << 32);
+        __syncthreads();
+        const long long n2 = block_scan_lds(toff, toff, E, red2);
+        ns = (int)(n2 & 0xFFFFFFFFll);
+        nb = (int)(n2 >> 32);
+    }
     if (key < (uint32_t)E) {
         int r = __popcll(m & lanes_below());
         for (int w = 0; w < wave; ++w) r += wcnt[w][key];
@@ -179,29 +197,20 @@ __global__ __launch_bounds__(kBkChunk) void bucket_scatter_kernel(
         pos[s] = p;
     }
     if (chunk != 0) return;
-    // chunk 0: counts, offsets and the tile lists (wcnt is reused once every
-    // thread has placed its pair)
-    const bool all = all_small_tiles(S, E);
-    __syncthreads();
-    for (int e = tid; e < E; e += kBkChunk) {
-        counts[e] = tot[e];
-        offsets[e] = off_l[e];
-        wcnt[0][e] = small_tiles_of(tot[e], all);
-        wcnt[1][e] = gemm_tiles_of(tot[e], all);
-    }
-    if (tid == 0) offsets[E] = S;
-    __syncthreads();
-    const int ns = block_scan_lds(wcnt[0], wcnt[2], E, red);
-    const int nb = block_scan_lds(wcnt[1], wcnt[3], E, red);
+    // chunk 0: counts, offsets and the tile lists
     for (int e = tid; e < E; e += kBkChunk) {
         const int c = tot[e], off = off_l[e];
+        counts[e] = c;
+        offsets[e] = off;
         const int nsm = small_tiles_of(c, all), nbg = gemm_tiles_of(c, all);
+        const int so = (int)(toff[e] & 0xFFFFFFFFll), bo = (int)(toff[e] >> 32);
         for (int i = 0; i < nbg; ++i)
-            big_tiles[wcnt[3][e] + i] = make_int4(e, off + i * kGemmM, min(kGemmM, c - i * kGemmM), 0);
+            big_tiles[bo + i] = make_int4(e, off + i * kGemmM, min(kGemmM, c - i * kGemmM), 0);
         for (int i = 0; i < nsm; ++i)
-            tiles[wcnt[2][e] + i] = make_int4(e, off + i * kTileM, min(kTileM, c - i * kTileM), 0);
+            tiles[so + i] = make_int4(e, off + i * kTileM, min(kTileM, c - i * kTileM), 0);
     }
     if (tid == 0) {
+        offsets[E] = S;
         n_tiles[0] = ns;
         n_tiles[1] = nb;
     }
