@@ -112,8 +112,8 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
  * Asynchronous on stream: nothing waits on the host, except that a T above
  * the reserved capacity first grows the workspace (a device synchronisation).
  * Non-finite inputs give unspecified routing and outputs.
- * Errors: INVALID_SHAPE (T < 1, or T so large that T*2*hidden_dim or
- * T*k*2*moe_intermediate reaches 2^32), INVALID_ARG (null/host pointers, out
+ * Errors: INVALID_SHAPE (T < 1, or T so large that T*4*hidden_dim or
+ * T*k*4*moe_intermediate reaches 2^32), INVALID_ARG (null/host pointers, out
  * overlapping x, bad handle), OOM, DEVICE. */
 moe_status moe_ffn_forward(moe_ffn_t h, int32_t T, const float *x, float *out, float *router_out,
                            int32_t *router_idx, void *stream);

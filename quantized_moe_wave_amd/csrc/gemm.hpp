@@ -40,7 +40,9 @@
 // of a tile run together and share its activation rows through the XCD's L2;
 // tiles are in expert order, so the tiles of one expert share its weights.
 //
-// Data movement, all by direct global->LDS loads (no staging registers):
+// Data movement, all by direct global->LDS loads (no staging registers), as
+// raw buffer loads: each lane's fixed byte offset in a VGPR, the per-step
+// offset in an SGPR, so no load costs address VALU in the main loop:
 //   A (staged activations): a ring of 4 chunk buffers; chunk c = 4b + q is a
 //   quarter super-block (2 k-steps = 256 bytes of each row); 16-byte slot j
 //   of row r is stored at slot j ^ (r % 16), so that the 16 lanes reading one
@@ -141,6 +143,19 @@ __device__ __forceinline__ void load_lds4(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
 }
 
+// Raw buffer loads into LDS: a buffer resource over base (stride 0, all of
+// the first 4 GB valid; dword 3 = the gfx9 raw 32-bit format), a per-lane
+// 32-bit byte offset and a uniform one (an SGPR: no per-load address VALU).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, -1, 0x00020000);
+}
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void bload_lds4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff, void *lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 4, voff, soff, 0, 0);
+}
+
 // s_waitcnt vmcnt(N) only (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
 // expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
@@ -192,16 +207,18 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     // ---- per-lane load offsets
     // A (halves): rows 4*(kALoads*wave + i) + lane/16, slot (lane%16) ^ (row%16)
     // (staged rows stay far below 2^32 halves)
-    uint32_t arow_o[kALoads];
+    uint32_t arow_o[kALoads];  // bytes
 #pragma unroll
     for (int i = 0; i < kALoads; ++i) {
         const int r = 4 * kALoads * wave + 4 * i + (lane >> 4);
         const int sl = (lane & 15) ^ (r & 15);
-        arow_o[i] = (uint32_t)src_row(r) * (uint32_t)(2 * K) + (uint32_t)sl * 8u;
+        arow_o[i] = (uint32_t)src_row(r) * (uint32_t)(4 * K) + (uint32_t)sl * 16u;
     }
+    const __amdgpu_buffer_rsrc_t rs_a = buf_rsrc(a_hilo);
     // Bq: flat 16-byte slot f = (wave*kBLoads + i)*64 + lane of a half
     // super-block -> group f/64, 16-byte slot f%64 of its 1 KB
     const uint8_t *wtile = W + ((size_t)e * ngroups + rg0) * nsb * kGroupSbBytes;
+    const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(wtile);
     uint32_t boff[kBLoads];
 #pragma unroll
     for (int i = 0; i < kBLoads; ++i) {
@@ -219,36 +236,39 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     }
     // k-step sums: XsNarrow: row 8*wave + lane/8, 4-byte piece lane%8;
     // else row 32*(wave%2) + lane/2, 16-byte half lane%2
-    const f16 *xs_p = Sh::XsNarrow ? a_xs + (size_t)src_row(8 * wave + (lane >> 3)) * nsb * 16 + (lane & 7) * 2
-                                   : a_xs + (size_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8;
+    const uint32_t xs_o = 2u * (Sh::XsNarrow ? (uint32_t)src_row(8 * wave + (lane >> 3)) * nsb * 16 + (lane & 7) * 2
+                                             : (uint32_t)src_row(32 * (wave & 1) + (lane >> 1)) * nsb * 16 + (lane & 1) * 8);
+    const __amdgpu_buffer_rsrc_t rs_xs = buf_rsrc(a_xs);
+    const uint32_t dx_o = Q8 ? (uint32_t)src_row(lane) * nsb * 4u : 0u;
+    const __amdgpu_buffer_rsrc_t rs_dx = buf_rsrc(a_sinv);
 
     auto issue_a = [&](int c) {  // chunk c into ring slot c % 4   (kALoads loads)
         const int b = c >> 2, q = c & 3;
         uint8_t *dst = abuf + (c & (kGemmRing - 1)) * Sh::ABuf + (4 * kALoads * wave) * kChunkBytes;
 #pragma unroll
-        for (int i = 0; i < kALoads; ++i) load_lds16(a_hilo + arow_o[i] + b * 512 + q * 128, dst + i * 1024);
+        for (int i = 0; i < kALoads; ++i) bload_lds16(rs_a, arow_o[i], (uint32_t)(b * 1024 + q * 256), dst + i * 1024);
     };
     auto issue_bq = [&](int hs) {  // quants of half super-block hs into slot hs % 2   (kBLoads loads)
         uint8_t *dst = bqbuf + (hs & 1) * Sh::BqBuf + wave * kBLoads * 1024;
-        const size_t src = (size_t)(hs >> 1) * kGroupSbBytes + (hs & 1) * 1024;
+        const uint32_t src = (uint32_t)((hs >> 1) * kGroupSbBytes + (hs & 1) * 1024);
 #pragma unroll
-        for (int i = 0; i < kBLoads; ++i) load_lds16(wtile + boff[i] + src, dst + i * 1024);
+        for (int i = 0; i < kBLoads; ++i) bload_lds16(rs_w, boff[i], src, dst + i * 1024);
     };
     auto issue_hx = [&](int b) {  // headers + k-step sums (+ Q8 row scales) of super-block b into buffer b % 2   (kHxLoads loads)
         uint8_t *dst = hbuf + (b & 1) * Sh::HdrBuf + wave * kHdrLoads * 64 * kHdrB;
 #pragma unroll
         for (int i = 0; i < kHdrLoads; ++i) {
             if (kHdrB == 16)
-                load_lds16(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 1024);
+                bload_lds16(rs_w, hoff[i], (uint32_t)(b * kGroupSbBytes), dst + i * 1024);
             else
-                load_lds4(wtile + hoff[i] + (size_t)b * kGroupSbBytes, dst + i * 256);
+                bload_lds4(rs_w, hoff[i], (uint32_t)(b * kGroupSbBytes), dst + i * 256);
         }
         if (Sh::XsNarrow)
-            load_lds4(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 256);
+            bload_lds4(rs_xs, xs_o, (uint32_t)(b * 32), xsbuf + (b & 1) * Sh::XsBuf + wave * 256);
         else
-            load_lds16(xs_p + b * 16, xsbuf + (b & 1) * Sh::XsBuf + wave * 1024);
+            bload_lds16(rs_xs, xs_o, (uint32_t)(b * 32), xsbuf + (b & 1) * Sh::XsBuf + wave * 1024);
         if (Q8)  // the tile rows' scales of super-block b (row lane), one copy per wave
-            load_lds4(a_sinv + (size_t)src_row(lane) * nsb + b, dxbuf + (b & 1) * (Sh::DxBuf / 4) + wave * 64);
+            bload_lds4(rs_dx, dx_o, (uint32_t)(b * 4), dxbuf + (b & 1) * (Sh::DxBuf / 4) + wave * 64);
     };
 
     // ---- sub-block scales of this lane's CW weight groups (row n) for the

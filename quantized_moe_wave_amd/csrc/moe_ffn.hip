@@ -353,9 +353,9 @@ moe_status check_call(moe_ffn_t h, int32_t T, const float *x, float *out, float 
     if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "token count must be >= 1 (got %d)", T);
     const moe_ffn_shape &s = h->sh;
     const int k = s.num_experts_per_tok, H = s.hidden_dim, I = s.moe_intermediate;
-    // staged rows are addressed with 32-bit half offsets
-    if ((uint64_t)T * 2 * H >= (1ull << 32) || (uint64_t)T * k * 2 * I >= (1ull << 32))
-        return fail(MOE_ERR_INVALID_SHAPE, "token count %d too large for this layer (T*2*H and T*k*2*I must be < 2^32)",
+    // the grouped GEMMs address staged rows with 32-bit byte offsets
+    if ((uint64_t)T * 4 * H >= (1ull << 32) || (uint64_t)T * k * 4 * I >= (1ull << 32))
+        return fail(MOE_ERR_INVALID_SHAPE, "token count %d too large for this layer (T*4*H and T*k*4*I must be < 2^32)",
                     T);
     if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x and out must not be NULL");
     if (!is_device_ptr(x) || !is_device_ptr(out) || (router_out && !is_device_ptr(router_out)) ||

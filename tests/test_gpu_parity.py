@@ -176,6 +176,13 @@ def test_error_returns():
     st = _lib.moe_ffn_forward(_vp(layer.handle), 4, xh.ctypes.data_as(ctypes.c_void_p),
                               ctypes.c_void_p(torch.empty_like(x).data_ptr()), None, None, None)
     assert st == 2
+    # token counts whose staged activations pass 4 GiB (T*4*hidden_dim >= 2^32 at hidden 256, k = 2, I = 256):
+    # rejected before any pointer is read or any workspace is sized
+    for T in (1 << 22, (1 << 21) + 1):
+        ok = T * 4 * 256 < (1 << 32) and T * 2 * 4 * 256 < (1 << 32)
+        st = _lib.moe_ffn_forward(_vp(layer.handle), T, ctypes.c_void_p(x.data_ptr()),
+                                  ctypes.c_void_p(torch.empty_like(x).data_ptr()), None, None, None)
+        assert not ok and st == 1, (T, st)
     # the layer still works after the rejected calls
     g = parity.run_gpu(layer, x)
     parity.check_parity(inp, g)
