@@ -1,22 +1,28 @@
 // Host side of the C ABI declared in include/moe_ffn.h: validation, weight
 // repack, workspace, and the per-call launch sequence.
 //
-// forward(T) enqueues, all on the caller's stream, with no host wait:
-//   1. router_kernel   logits (fp64), top-k, renormalised weights (a few
-//                      tokens), or router_logits_kernel + topk_kernel
+// forward(T) enqueues, all on the caller's stream, with no host wait (T <= 4
+// with shapes that fit: the three decode launches of decode.hpp instead):
+//   1. router_kernel   logits (fp64), top-k, renormalised weights (T <= 4
+//                      outside the decode path), or router_logits_kernel +
+//                      topk_token_kernel (topk_kernel for rows longer than
+//                      16 super-blocks), the latter also staging the x rows
 //   2. bucket_single_kernel (one workgroup; up to 4096 pairs over at most
 //                      256 experts), else bucket_hist_kernel +
 //                      bucket_scatter_kernel: stable counting sort of
 //                      (token, slot) by expert + tiles
-//   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums
+//   3. stage_kernel    x rows -> scaled fp16 hi/lo + sub-block sums (only
+//                      where step 1 did not stage them)
 //   4. expert GATEUP   gate/up Q4_K MFMA + SiLU(g)*u -> h[slot][I]
 //   5. stage_kernel    h rows -> staged
 //   6. expert DOWN     down Q4_K MFMA -> Y[slot][H]
 //   7. combine_kernel  out[t] = sum_j w[t][j] * Y[pos[t][j]]
-// forward_block(T) first runs rmsnorm_kernel (hidden -> normalised rows in the
-// workspace), then the same sequence on those rows, the last kernel adding
-// hidden to its output; on the decode path the router launch normalises the
-// values it reads instead (no norm launch).
+// forward_block(T) folds the pre-FFN RMSNorm into the router launches (decode:
+// the router launch normalises the values it reads; general path: the router
+// sums W_r . (x * g) and the top-k launch applies 1/rms and stages the
+// normalised row), or, where that does not fit, first runs rmsnorm_kernel
+// (hidden -> normalised rows in the workspace); the last kernel adds hidden
+// to its output.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 

@@ -17,6 +17,9 @@
 // top-k choice is exact except for true near-ties.
 // The last workgroup of a token group to finish (device-scope counter) runs
 // the softmax/top-k for that group's tokens, one wave per token.
+// That is router_kernel, for T <= 4 outside the decode path; more tokens take
+// router_logits_kernel (fp64 MFMA tiles) and a top-k launch of their own
+// (topk_token_kernel, or topk_kernel for long rows), below.
 #pragma once
 #include "common.hpp"
 #include "norm.hpp"
@@ -328,7 +331,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // Split of H over blockIdx.z for small T: workgroup z covers columns
 // [z*H/ks, (z+1)*H/ks) and writes its partial sums to part[z][T][E] (the
-// bias in z = 0); topk_kernel adds the ks partials in z order. ks = 1 writes
+// bias in z = 0); the top-k launch adds the ks partials in z order. ks = 1 writes
 // the logits directly. H/ks must be a multiple of 64 * NWV (each wave's share
 // a whole number of kRlPf 16-column groups).
 constexpr int kRlMaxSplit = 16;
@@ -336,7 +339,7 @@ constexpr int kRlPartDoubles = 256 * 1024;  // ks*T*E < 1024 * 256 for the ks th
 
 // NORM (the block's pre-FFN RMSNorm folded in, norm_w = its weight g): the
 // kernel sums W_r[e] . (x * g) (each product x*g exact in double) and leaves
-// the row's 1/rms factor, and the bias, to topk_kernel, which has the row:
+// the row's 1/rms factor, and the bias, to the top-k launch, which has the row:
 // logit = (1/rms) * sum + bias. Equal to the sum over the rounded normalised
 // row up to the rounding of its elements (a few 1e-8 of a logit).
 template <int NWV, bool NORM>
