@@ -251,7 +251,7 @@ def test_many_experts(T):
 def test_experts_up_to_256(E, T):
     """128 < E <= 256: the widest rank selection (every candidate counts 256
     keys; E = 256 uses the whole 8-bit index field of the key), on the decode
-    path (T = 3) and the general path (T = 40)."""
+    path (T = 3) and the general path (T = 40), for the layer and the block."""
     print(f"[parity] E={E} k=8 T={T}", flush=True)
     import dataclasses
 
@@ -262,6 +262,18 @@ def test_experts_up_to_256(E, T):
     layer, dev = parity.make_layer(inp)
     inp2, g = _run(inp, layer, _x(inp, T, seed=50 + T))
     parity.check_parity(inp2, g)
+    # the block too: on the general path its norm folds into the top-k launch's widest ranking
+    import torch
+
+    import oracle
+
+    hidden = (_s.gen_x(4, 11, T, wl.hidden) * np.float32(3.0)).astype(np.float32)
+    gn = _s.gen_norm(4, 0, wl.hidden)
+    layer.set_norm(torch.from_numpy(gn), _s.NORM_EPS)
+    run = parity.run_gpu(layer, torch.from_numpy(hidden).cuda(), block=True)
+    xn = oracle.rms_norm(hidden, gn, _s.NORM_EPS).astype(np.float32)
+    parity.check_parity(_s.LayerInputs(wl.with_tokens(T), xn, inp.router, inp.bias, inp.gate, inp.up, inp.down), run,
+                        resid=hidden)
     layer.close()
 
 
