@@ -109,6 +109,10 @@ moe_status moe_ffn_reserve(moe_ffn_t h, int32_t max_tokens, void *stream);
  * Expert choice: the k largest logits; equal logits go to the lower expert
  * index. Results are bitwise reproducible from call to call (no floating-point
  * atomics; every sum has a fixed order).
+ * Paths: T <= 4 with num_experts <= 256, hidden_dim <= 4096 and
+ * num_experts_per_tok * moe_intermediate / 256 <= 384 take the decode path
+ * (three launches: router, gate/up per pair, down and combine); other calls
+ * the bucketed path (router, top-k, bucketing, grouped GEMMs, combine).
  * Asynchronous on stream: nothing waits on the host, except that a T above
  * the reserved capacity first grows the workspace (a device synchronisation).
  * Non-finite inputs give unspecified routing and outputs.
@@ -144,7 +148,7 @@ moe_status moe_ffn_forward_noalloc(moe_ffn_t h, int32_t T, const float *x, float
  * enter the expert matvecs as codes q and a scale d per 256 values, amax =
  * max |v|, q = rint(v * (127 / amax)) in [-127, 127], d = amax / 127, all in
  * fp32; the router runs on the fp32 x. Arguments, outputs, token counts and
- * errors as moe_ffn_forward (the same paths: a decode path for T <= 4 and the
+ * errors as moe_ffn_forward (the same paths: the decode path and the
  * bucketed grouped GEMMs, there in one MFMA pass on the codes, each output in
  * units of the row's d per super-block). Non-finite inputs give unspecified
  * outputs. */
@@ -168,12 +172,11 @@ moe_status moe_ffn_set_norm(moe_ffn_t h, const float *norm_w, float eps, void *s
  * standard RMSNorm; the pages name the op without its formula), rounded to
  * fp32 as the layer's input, and the residual add of the block after the MoE
  * FFN (forward_qwen3_moe.rs: the "Residual" step after prefill step 2g,
- * decode step 2i). On the decode path (T <= 4 and the shapes listed for
- * moe_ffn_forward_q8) the norm is fused into the router launch; on the
- * bucketed path (T > 4) into the router and top-k launches when
- * num_experts <= 256 and hidden_dim <= 4096; otherwise it is a launch of its
- * own ahead of the layer. The residual add happens in the kernel that writes
- * out.
+ * decode step 2i). On the decode path (see moe_ffn_forward) the norm is
+ * fused into the router launch; on the bucketed path with T > 4 into the
+ * router and top-k launches when num_experts <= 256 and hidden_dim <= 4096;
+ * otherwise it is a launch of its own ahead of the layer. The residual add
+ * happens in the kernel that writes out.
  *   hidden      [T][H] fp32 residual stream.
  *   out         [T][H] fp32 block output. Must not overlap hidden.
  *   router_out, router_idx, stream: as for moe_ffn_forward (routing of the
