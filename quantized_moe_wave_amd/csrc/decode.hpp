@@ -579,11 +579,41 @@ __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     }
     __syncthreads();
     if (wave == 0) {
+        // o = sum over slots j in slot order of w_j * y_j, y_j = slot j's sum
+        // over its super-blocks in super-block order (column lane % 16)
+        const int n16 = lane & 15;
         float o = 0.f;
-        for (int j = 0; j < k; ++j) {
-            float y = 0.f;
-            for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][lane & 15];
-            o += __shfl(my_w, j, kWave) * y;
+        if (k <= 8 && nsb <= 8) {
+            // every read issued together: lane group jg = lane / 16 sums slots
+            // jg and jg + 4 (entries past k or nsb read a valid entry and are
+            // replaced by +0, which leaves each sum's bits unchanged)
+            const int jg = lane >> 4;
+            float ys[2];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int j = 4 * r + jg;
+                float pv[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b) pv[b] = part[min(j, k - 1) * nsb + min(b, nsb - 1)][n16];
+                float y = 0.f;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) y += (j < k && b < nsb) ? pv[b] : 0.f;
+                ys[r] = y;
+            }
+            float wv[8], yv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                wv[j] = __shfl(my_w, j, kWave);  // 0 past k (my_w of lanes >= k)
+                yv[j] = __shfl(ys[j >> 2], (j & 3) * 16 + n16, kWave);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o += wv[j] * (j < k ? yv[j] : 0.f);
+        } else {
+            for (int j = 0; j < k; ++j) {
+                float y = 0.f;
+                for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][n16];
+                o += __shfl(my_w, j, kWave) * y;
+            }
         }
         if (lane < 16) {
             const size_t oi = (size_t)t * H + rg * kRowGroup + lane;
