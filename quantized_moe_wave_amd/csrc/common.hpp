@@ -61,11 +61,32 @@ __device__ __forceinline__ void lds_wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Wave-wide reductions (64 lanes).
+// DPP moves within rows of 16 lanes (gfx9 dpp_ctrl encodings): quad_perm
+// [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2), row_half_mirror
+// (lane i of each 8 <-> 7 - i), row_mirror (lane i of each 16 <-> 15 - i),
+// row_ror 8 (lane ^ 8 within 16). A register-to-register move, where a
+// shuffle through ds_bpermute costs an LDS round trip.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140, kDppXor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Largest value of this lane's row of 16, on every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<kDppXor1>(v));
+    v = fmaxf(v, dpp_f<kDppXor2>(v));
+    v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+    return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+
+// Wave-wide reductions (64 lanes; every lane must be active). wave_max: the
+// four row maxima combined from lanes 0, 16, 32, 48.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    v = row16_max(v);
+    return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
 }
 
 __device__ __forceinline__ double wave_sum(double v) {

@@ -450,173 +450,210 @@ __global__ __launch_bounds__(kGpWaves * 64) void gateup_pair_kernel(const uint8_
     float r = red[0][lane][0];
 #pragma unroll
     for (int w = 1; w < kGpWaves; ++w) r += red[w][lane][0];
-    const float u = __shfl_xor(r, 8, kWave);
+    const float u = dpp_f<kDppXor8>(r);
     if (lane < 8) h[(size_t)p * I + rg * 8 + lane] = silu_f(r) * u;
 }
 
-constexpr int kDcWaves = 12;       // waves per down/combine workgroup
-constexpr int kDcMaxUnits = 2;     // (slot, super-block) units a wave holds in flight
+constexpr int kDcWaves = 8;        // waves per down/combine workgroup
+constexpr int kDcMaxPairs = 2;     // unit pairs a wave holds in flight
 
-// Grid (H/16 row groups + 1, T tokens), kDcWaves waves. The token's experts and
-// router weights come from gateup_pair_kernel (dsel, dw). The k*nsb (slot j,
-// super-block b) units of one token are spread over the waves; each unit
-// stages its 256 h values (row t*k + j of gateup_pair_kernel's output) in LDS (power-of-two scale, fp16 hi/lo, sub-block
-// sums), runs the row-0 MFMA tile against the down weights of expert idx[t][j]
-// and leaves a 16-column partial in LDS. Then out[t][cols] =
-// sum_j w[t][j] * sum_b partial[j][b] in slot order.
+// Grid (2 * H/16 half row groups + 1, T tokens), kDcWaves waves. Workgroup x
+// computes rows 8 (x % 2) .. 8 (x % 2) + 7 of row group x / 2 for token t. The
+// token's experts and router weights come from gateup_pair_kernel (dsel, dw).
+// The k*nsb (slot j, super-block b) units of the token go in pairs (2P, 2P+1)
+// to the waves; a wave stages both units' 256 h values (row t*k + j of
+// gateup_pair_kernel's output) in LDS (power-of-two scale, fp16 hi/lo,
+// sub-block sums) and runs one MFMA tile for the pair: A rows 0 and 1 are the
+// two units' staged h, B columns 0-7 the 8 weight rows of the first unit's
+// expert and super-block, columns 8-15 those of the second's, so C[0][0..7]
+// and C[1][8..15] are the two units' partials (each element the same sum as a
+// tile of its own: an output element depends on its row and column only).
+// Two half row groups per row group use every CU at the 30b shape (257
+// workgroups of one pair per wave instead of 129 of two units per wave).
+// Then out[t][rows] = sum_j w[t][j] * sum_b partial[j][b] in slot order.
 __global__ __launch_bounds__(kDcWaves * 64) void down_combine_small_kernel(
     const uint8_t *__restrict__ Wd, int ngroups, int nsb, const double *__restrict__ logits, int E, int T, int k,
     const float *__restrict__ h, int I, const int32_t *__restrict__ dsel, const float *__restrict__ dw,
     const float *__restrict__ resid, float *__restrict__ out, int H, int32_t *__restrict__ idx_out,
     float *__restrict__ w_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ entries, int32_t *__restrict__ pos, int q8) {
-    const int rg = blockIdx.x, t = blockIdx.y;
+    const int x = blockIdx.x, t = blockIdx.y;
+    const int rg = x >> 1, hf = x & 1;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int units = k * nsb;
-    __shared__ float part[kMaxTopK * 6][16];
-    __shared__ __attribute__((aligned(16))) f16 afrag[kDcWaves][8 * 4 * 16];  // [k-step][g][hi 8 | lo 8]
-    __shared__ __attribute__((aligned(16))) f16 axs[kDcWaves][16];
-    __shared__ float asinv[kDcWaves];
+    const int units = k * nsb, npairs = (units + 1) >> 1;
+    __shared__ float part[kMaxTopK * 6][8];
+    // per wave: the current pair's two staged h blocks [k-step][g][hi 8 |
+    // lo 8], their sub-block sums and 1/s (reused pair after pair)
+    __shared__ __attribute__((aligned(16))) f16 afrag[kDcWaves][2][8 * 4 * 16];
+    __shared__ __attribute__((aligned(16))) f16 axs[kDcWaves][2][16];
+    __shared__ float asinv[kDcWaves][2];
     __shared__ __attribute__((aligned(16))) double lg[kRankMaxExperts];
     __shared__ int sel_e[kMaxTopK];
     __shared__ double sel_v[kMaxTopK];
 
-    // The extra column of workgroups (rg == H/16) has no down rows: the first
-    // one writes the routing outputs of all T tokens, the others leave.
-    if (rg == ngroups) {
+    // The last workgroup of each token column (x == 2 * ngroups) has no down
+    // rows: the first one writes the routing outputs of all T tokens, the
+    // others leave.
+    if (x == 2 * ngroups) {
         if (t == 0)
             routing_outputs_small(logits, T, E, k, lg, sel_e, sel_v, idx_out, w_out, counts, offsets, entries, pos);
         return;
     }
+    // unit v of pair slot i, unit half uh (0, 1) of this pass: clamped to a
+    // valid unit (a missing second unit of an odd count repeats the first and
+    // its result is dropped)
+    auto unit_of = [&](int base, int i, int uh) {
+        const int P = min(base + i * kDcWaves + wave, npairs - 1);
+        return min(2 * P + uh, units - 1);
+    };
     // h rows are pair-indexed (t*k + j), so the first pass's h loads do not
-    // wait for the routing: issued here, they are in flight with its loads
-    float4 hv0[kDcMaxUnits];
+    // wait for the routing: issued here, they are in flight with its loads.
+    // Lane holds columns 4*lane .. +3 of each unit's super-block.
+    float4 hv0[kDcMaxPairs][2];
 #pragma unroll
-    for (int i = 0; i < kDcMaxUnits; ++i) {
-        const int u = min(i * kDcWaves + wave, units - 1);
-        const int j = u / nsb, b = u % nsb;
-        hv0[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
-    }
+    for (int i = 0; i < kDcMaxPairs; ++i)
+#pragma unroll
+        for (int uh = 0; uh < 2; ++uh) {
+            const int u = unit_of(0, i, uh);
+            const int j = u / nsb, b = u % nsb;
+            hv0[i][uh] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
+        }
     // the token's k experts and renormalised weights, lane j holding slot j,
     // as gateup_pair_kernel ranked them (loaded together with the h rows)
     const int my_e = dsel[(size_t)t * k + min(lane, k - 1)];
     const float my_w = lane < k ? dw[(size_t)t * k + lane] : 0.f;
-    for (int base = 0; base < units; base += kDcWaves * kDcMaxUnits) {
-        u32x4 q0[kDcMaxUnits], q1[kDcMaxUnits], hdr[kDcMaxUnits];
-        float4 hv[kDcMaxUnits];
+    // this lane's weight row within the group, and which unit of a pair its
+    // column belongs to
+    const int wrow = hf * 8 + (n & 7), mine = n >> 3;
+    for (int base = 0; base < npairs; base += kDcWaves * kDcMaxPairs) {
+        u32x4 q0[kDcMaxPairs], q1[kDcMaxPairs], hdr[kDcMaxPairs];
+        float4 hv[kDcMaxPairs][2];
 #pragma unroll
-        for (int i = 0; i < kDcMaxUnits; ++i) {
-            const int u = min(base + i * kDcWaves + wave, units - 1);  // clamped: loads stay unconditional
+        for (int i = 0; i < kDcMaxPairs; ++i) {
+            // loads unconditional (clamped): B column n of this lane is weight
+            // row wrow of unit `mine` of the pair
+            const int u = unit_of(base, i, mine);
             const int j = u / nsb, b = u % nsb;
             const int e = __shfl(my_e, j, kWave);
             const uint8_t *blk = Wd + ((size_t)((size_t)e * ngroups + rg) * nsb + b) * kGroupSbBytes;
-            q0[i] = *(const u32x4 *)(blk + lane * 16);
-            q1[i] = *(const u32x4 *)(blk + 1024 + lane * 16);
-            hdr[i] = *(const u32x4 *)(blk + kGroupQsBytes + n * 16);
-            if (base == 0)
-                hv[i] = hv0[i];
-            else
-                hv[i] = *(const float4 *)(h + ((size_t)t * k + j) * I + b * kQ4Weights + lane * 4);
+            q0[i] = *(const u32x4 *)(blk + (g * 16 + wrow) * 16);
+            q1[i] = *(const u32x4 *)(blk + 1024 + (g * 16 + wrow) * 16);
+            hdr[i] = *(const u32x4 *)(blk + kGroupQsBytes + wrow * 16);
+#pragma unroll
+            for (int uh = 0; uh < 2; ++uh) {
+                if (base == 0) {
+                    hv[i][uh] = hv0[i][uh];
+                } else {
+                    const int uu = unit_of(base, i, uh);
+                    hv[i][uh] = *(const float4 *)(h + ((size_t)t * k + uu / nsb) * I + (uu % nsb) * kQ4Weights +
+                                                  lane * 4);
+                }
+            }
         }
 #pragma unroll
-        for (int i = 0; i < kDcMaxUnits; ++i) {
-            const int u = base + i * kDcWaves + wave;
-            if (u >= units) break;
-            // stage: lane holds columns 4*lane .. +3 of this super-block
-            float v[4] = {hv[i].x, hv[i].y, hv[i].z, hv[i].w};
-            float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-            m = wave_max(m);
-            int ex = 0;
-            if (m > 0.f) (void)frexpf(m, &ex);
-            int se = 10 - ex;
-            se = se > 100 ? 100 : (se < -100 ? -100 : se);
-            if (!(m > 0.f) || !(m < INFINITY)) se = 0;
-            if (q8) {  // Q8_K codes of this 256-value block of h (q8_code), staged with scale 1
-                const float is = m > 0.f ? 127.f / m : 0.f;
+        for (int i = 0; i < kDcMaxPairs; ++i) {
+            const int P = base + i * kDcWaves + wave;
+            if (P >= npairs) break;
+            // stage both units of the pair
 #pragma unroll
-                for (int c = 0; c < 4; ++c) v[c] = q8_code(v[c], is);
-                se = 0;
-            }
-            const float scl = ldexpf(1.f, se);
-            const int s = lane >> 3, gg = (lane & 7) >> 1, half = lane & 1;
-            float part_sum = 0.f;
-            f16 *fr = &afrag[wave][(s * 4 + gg) * 16];
+            for (int uh = 0; uh < 2; ++uh) {
+                float v[4] = {hv[i][uh].x, hv[i][uh].y, hv[i][uh].z, hv[i][uh].w};
+                float m = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                m = wave_max(m);
+                int ex = 0;
+                if (m > 0.f) (void)frexpf(m, &ex);
+                int se = 10 - ex;
+                se = se > 100 ? 100 : (se < -100 ? -100 : se);
+                if (!(m > 0.f) || !(m < INFINITY)) se = 0;
+                if (q8) {  // Q8_K codes of this 256-value block of h (q8_code), staged with scale 1
+                    const float is = m > 0.f ? 127.f / m : 0.f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const float y = v[c] * scl;
-                const f16 hi = (f16)y;
-                const int el = perm8(4 * half + c);
-                fr[el] = hi;
-                fr[8 + el] = (f16)(y - (float)hi);
-                part_sum += y;
+                    for (int c = 0; c < 4; ++c) v[c] = q8_code(v[c], is);
+                    se = 0;
+                }
+                const float scl = ldexpf(1.f, se);
+                const int s = lane >> 3, gg = (lane & 7) >> 1, half = lane & 1;
+                float part_sum = 0.f;
+                f16 *fr = &afrag[wave][uh][(s * 4 + gg) * 16];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float y = v[c] * scl;
+                    const f16 hi = (f16)y;
+                    const int el = perm8(4 * half + c);
+                    fr[el] = hi;
+                    fr[8 + el] = (f16)(y - (float)hi);
+                    part_sum += y;
+                }
+                // the 8 lanes of the k-step: lane ^ 1, lane ^ 2, then the other
+                // quad (same sums, in the same order, as shuffles by xor)
+                part_sum += dpp_f<kDppXor1>(part_sum);
+                part_sum += dpp_f<kDppXor2>(part_sum);
+                part_sum += dpp_f<kDppHalfMirror>(part_sum);
+                if ((lane & 7) == 0) {
+                    const f16 hs = (f16)part_sum;
+                    axs[wave][uh][s] = hs;
+                    axs[wave][uh][8 + s] = (f16)(part_sum - (float)hs);
+                }
+                if (lane == 0) asinv[wave][uh] = q8 ? m / 127.f : ldexpf(1.f, -se);
             }
-            part_sum += __shfl_xor(part_sum, 1, kWave);
-            part_sum += __shfl_xor(part_sum, 2, kWave);
-            part_sum += __shfl_xor(part_sum, 4, kWave);
-            if ((lane & 7) == 0) {
-                const f16 hs = (f16)part_sum;
-                axs[wave][s] = hs;
-                axs[wave][8 + s] = (f16)(part_sum - (float)hs);
-            }
-            if (lane == 0) asinv[wave] = q8 ? m / 127.f : ldexpf(1.f, -se);
             lds_wave_sync();
 
-            const bool a_ok = (n == 0);
+            // A rows 0 and 1: the pair's two units; other rows zero
+            const bool a_ok = n < 2;
             auto afr = [&](int ss, f16x8 &hi, f16x8 &lo) {
-                const f16x8 hv8 = *(const f16x8 *)&afrag[wave][(ss * 4 + g) * 16];
-                const f16x8 lv8 = *(const f16x8 *)&afrag[wave][(ss * 4 + g) * 16 + 8];
+                const f16 *ap = &afrag[wave][n & 1][(ss * 4 + g) * 16];
+                const f16x8 hv8 = *(const f16x8 *)ap;
+                const f16x8 lv8 = *(const f16x8 *)(ap + 8);
                 hi = a_ok ? hv8 : f16x8{};
                 lo = a_ok ? lv8 : f16x8{};
             };
-            const f16x4 amv = *(const f16x4 *)&axs[wave][4 * g];
-            const float sv[4] = {g == 0 ? asinv[wave] : 0.f, 0.f, 0.f, 0.f};
+            const f16x4 amv = *(const f16x4 *)&axs[wave][n & 1][4 * g];
+            const float sv[4] = {g == 0 ? asinv[wave][0] : 0.f, g == 0 ? asinv[wave][1] : 0.f, 0.f, 0.f};
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             mma_sb_fn(q0[i], q1[i], hdr[i], afr, a_ok ? amv : f16x4{}, sv, g, acc);
-            if (lane < 16) part[u][n] = acc[0];  // row 0, column n
+            // C[0][0..7] (unit 2P) and C[1][8..15] (unit 2P + 1, if it exists)
+            if (g == 0) {
+                const int u = 2 * P + mine;
+                if (u < units) part[u][n & 7] = mine ? acc[1] : acc[0];
+            }
             lds_wave_sync();
         }
     }
     __syncthreads();
     if (wave == 0) {
         // o = sum over slots j in slot order of w_j * y_j, y_j = slot j's sum
-        // over its super-blocks in super-block order (column lane % 16)
-        const int n16 = lane & 15;
+        // over its super-blocks in super-block order (row lane % 8)
+        const int r8 = lane & 7;
         float o = 0.f;
         if (k <= 8 && nsb <= 8) {
-            // every read issued together: lane group jg = lane / 16 sums slots
-            // jg and jg + 4 (entries past k or nsb read a valid entry and are
-            // replaced by +0, which leaves each sum's bits unchanged)
-            const int jg = lane >> 4;
-            float ys[2];
+            // every read issued together: lane group j = lane / 8 sums slot j
+            // (entries past k or nsb read a valid entry and are replaced by
+            // +0, which leaves each sum's bits unchanged)
+            const int j = lane >> 3;
+            float pv[8];
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int j = 4 * r + jg;
-                float pv[8];
+            for (int b = 0; b < 8; ++b) pv[b] = part[min(j, k - 1) * nsb + min(b, nsb - 1)][r8];
+            float y = 0.f;
 #pragma unroll
-                for (int b = 0; b < 8; ++b) pv[b] = part[min(j, k - 1) * nsb + min(b, nsb - 1)][n16];
-                float y = 0.f;
-#pragma unroll
-                for (int b = 0; b < 8; ++b) y += (j < k && b < nsb) ? pv[b] : 0.f;
-                ys[r] = y;
-            }
+            for (int b = 0; b < 8; ++b) y += (j < k && b < nsb) ? pv[b] : 0.f;
             float wv[8], yv[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                wv[j] = __shfl(my_w, j, kWave);  // 0 past k (my_w of lanes >= k)
-                yv[j] = __shfl(ys[j >> 2], (j & 3) * 16 + n16, kWave);
+            for (int jj = 0; jj < 8; ++jj) {
+                wv[jj] = __shfl(my_w, jj, kWave);  // 0 past k (my_w of lanes >= k)
+                yv[jj] = __shfl(y, jj * 8 + r8, kWave);
             }
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o += wv[j] * (j < k ? yv[j] : 0.f);
+            for (int jj = 0; jj < 8; ++jj) o += wv[jj] * (jj < k ? yv[jj] : 0.f);
         } else {
-            for (int j = 0; j < k; ++j) {
+            for (int jj = 0; jj < k; ++jj) {
                 float y = 0.f;
-                for (int b = 0; b < nsb; ++b) y += part[j * nsb + b][n16];
-                o += __shfl(my_w, j, kWave) * y;
+                for (int b = 0; b < nsb; ++b) y += part[jj * nsb + b][r8];
+                o += __shfl(my_w, jj, kWave) * y;
             }
         }
-        if (lane < 16) {
-            const size_t oi = (size_t)t * H + rg * kRowGroup + lane;
+        if (lane < 8) {
+            const size_t oi = (size_t)t * H + rg * kRowGroup + hf * 8 + lane;
             out[oi] = resid ? resid[oi] + o : o;  // resid: the block's residual add
         }
     }

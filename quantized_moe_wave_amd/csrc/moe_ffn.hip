@@ -501,7 +501,7 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
                w.logits, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, q8);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
-        launch(pf, kStDown, down_combine_small_kernel, dim3(H / kRowGroup + 1, T), dim3(kDcWaves * 64), st, h->dn,
+        launch(pf, kStDown, down_combine_small_kernel, dim3(2 * (H / kRowGroup) + 1, T), dim3(kDcWaves * 64), st, h->dn,
                H / kRowGroup, ni, w.logits, E, T, k, w.h, I, w.dsel, w.dw, resid, out, H, idx, wt, w.counts, w.offsets,
                w.entries, w.pos, q8);
         hipError_t e = hipGetLastError();

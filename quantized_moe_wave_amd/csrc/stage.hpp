@@ -93,8 +93,8 @@ __device__ __forceinline__ void stage_row_sb(const float *__restrict__ src, int 
 #pragma unroll
     for (int i = 0; i < 8; ++i) part += v[i] * sc;
     // sum of the 32 columns of k-step s: lanes 4s .. 4s+3
-    part += __shfl_xor(part, 1, kWave);
-    part += __shfl_xor(part, 2, kWave);
+    part += dpp_f<kDppXor1>(part);
+    part += dpp_f<kDppXor2>(part);
     if (lane < 32) {
         f16 *dst = hilo_row + (size_t)((b * 8 + s) * 4 + g) * 16;
         *(f16x8 *)dst = hi;
@@ -180,8 +180,8 @@ __device__ __forceinline__ void stage_emit(int b, float4 a, float4 c, float sc, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) part += v[i] * sc;
     // sum of the 32 columns of k-step s: lanes 4s .. 4s+3 of this half
-    part += __shfl_xor(part, 1, kWave);
-    part += __shfl_xor(part, 2, kWave);
+    part += dpp_f<kDppXor1>(part);
+    part += dpp_f<kDppXor2>(part);
     if (b < nsb) {
         f16 *dst = hilo_row + (size_t)((b * 8 + s) * 4 + g) * 16;
         *(f16x8 *)dst = hi;
@@ -246,9 +246,9 @@ __device__ __forceinline__ double staged_pairs_sumsq(const StagedPairs<SLOTS> &s
 
 // Largest value over the 32 lanes of this lane's half of the wave.
 __device__ __forceinline__ float half_wave_max(float m) {
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
-    return m;
+    m = row16_max(m);
+    const float lo = fmaxf(readlane_f(m, 0), readlane_f(m, 16)), hi = fmaxf(readlane_f(m, 32), readlane_f(m, 48));
+    return (threadIdx.x & 32) ? hi : lo;
 }
 
 // Q8_K-style codes of one super-block held as 8 columns per lane by a half

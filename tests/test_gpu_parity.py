@@ -332,3 +332,31 @@ def test_row_lengths(H, T):
     xn = oracle.rms_norm(hidden, gn, synth.NORM_EPS).astype(np.float32)
     inp_n = synth.LayerInputs(wl.with_tokens(T), xn, inp.router, inp.bias, inp.gate, inp.up, inp.down)
     parity.check_parity(inp_n, run, resid=hidden)
+
+
+@pytest.mark.parametrize("k,inter", [(3, 256), (1, 768), (3, 768)])
+def test_decode_odd_unit_counts(k, inter):
+    """Decode path (T <= 4) with an odd number of (slot, super-block) units, k * inter / 256 = 3, 3 and 9: the
+    down/combine launch pairs the units two per MFMA tile, so the last pair has one unit; the layer and the block."""
+    import dataclasses
+
+    import torch
+
+    import oracle
+
+    print(f"[parity] decode k={k} I={inter}", flush=True)
+    wl = dataclasses.replace(synth.WORKLOADS["tiny"], name=f"odd{k}_{inter}", top_k=k, inter=inter)
+    inp = synth.make_inputs(wl, seed=80 + k + inter // 256)
+    layer, dev = parity.make_layer(inp)
+    for T in (1, 4):
+        inp2, g = _run(inp, layer, _x(inp, T, seed=90 + T))
+        parity.check_parity(inp2, g)
+    T = 3
+    hidden = (synth.gen_x(5, 11, T, wl.hidden) * np.float32(3.0)).astype(np.float32)
+    gn = synth.gen_norm(5, 0, wl.hidden)
+    layer.set_norm(torch.from_numpy(gn), synth.NORM_EPS)
+    run = parity.run_gpu(layer, torch.from_numpy(hidden).cuda(), block=True)
+    layer.close()
+    xn = oracle.rms_norm(hidden, gn, synth.NORM_EPS).astype(np.float32)
+    parity.check_parity(synth.LayerInputs(wl.with_tokens(T), xn, inp.router, inp.bias, inp.gate, inp.up, inp.down), run,
+                        resid=hidden)
