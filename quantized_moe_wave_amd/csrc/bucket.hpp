@@ -53,11 +53,13 @@ __host__ __device__ inline int bucket_chunks(int S) { return (S + kBkChunk - 1) 
 constexpr int kBkKeyBits = 11; // keys 0..kMaxExperts (kMaxExperts: "no pair")
 static_assert(kMaxExperts < (1 << kBkKeyBits), "keys must fit the ballot match");
 
-// Lanes of this wave whose key equals this lane's (every lane must call it).
+// Lanes of this wave whose key equals this lane's, keys of NB bits (every
+// lane must call it).
+template <int NB = kBkKeyBits>
 __device__ __forceinline__ uint64_t lanes_with_key(uint32_t key) {
     uint64_t m = ~0ull;
 #pragma unroll
-    for (int b = 0; b < kBkKeyBits; ++b) {
+    for (int b = 0; b < NB; ++b) {
         const uint32_t bit = (key >> b) & 1u;
         const uint64_t set = __ballot(bit);
         m &= bit ? set : ~set;
@@ -258,6 +260,9 @@ __device__ __forceinline__ int bk1_scan(int v, int *red, int *total) {
 }
 
 // Grid: one workgroup of kBk1Waves * 64 threads; 1 <= S <= kBk1MaxPairs.
+// NB: key bits, 8 for E <= 255 (no pair = 255), 9 for E = 256 (no pair = 511):
+// the equal-key match costs one ballot per bit, per 64 pairs, in both passes.
+template <int NB>
 __global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
     const int32_t *__restrict__ idx, int S, int E, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ entries, int32_t *__restrict__ pos, int4 *__restrict__ tiles, int4 *__restrict__ big_tiles,
@@ -272,9 +277,10 @@ __global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
     uint32_t keys[kBk1MaxGroups];
 #pragma unroll
     for (int i = 0; i < kBk1MaxGroups; ++i) keys[i] = (uint32_t)idx[min(s0 + i * 64, S - 1)];
+    static_assert((1 << NB) - 1 >= kBk1MaxExperts - 1, "keys must fit");
 #pragma unroll
     for (int i = 0; i < kBk1MaxGroups; ++i)
-        if (!(i < G && s0 + i * 64 < S)) keys[i] = (uint32_t)kMaxExperts;
+        if (!(i < G && s0 + i * 64 < S)) keys[i] = (1u << NB) - 1u;  // no pair: above every expert of E < 2^NB
     for (int i = tid; i < kBk1Waves * kBk1MaxExperts; i += kBk1Waves * 64) (&wh[0][0])[i] = 0;
     __syncthreads();
     // pass 1: counts per (wave, expert)
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
     for (int i = 0; i < kBk1MaxGroups; ++i) {
         if (i < G) {
             const uint32_t key = keys[i];
-            const uint64_t m = lanes_with_key(key);
+            const uint64_t m = lanes_with_key<NB>(key);
             if (key < (uint32_t)E && (m & lanes_below()) == 0) wh[wave][key] += __popcll(m);
         }
     }
@@ -309,7 +315,7 @@ __global__ __launch_bounds__(kBk1Waves * 64) void bucket_single_kernel(
     for (int i = 0; i < kBk1MaxGroups; ++i) {
         if (i < G) {
             const uint32_t key = keys[i];
-            const uint64_t m = lanes_with_key(key);
+            const uint64_t m = lanes_with_key<NB>(key);
             if (key < (uint32_t)E) {
                 const int base = wh[wave][key];
                 const int p = base + __popcll(m & lanes_below());

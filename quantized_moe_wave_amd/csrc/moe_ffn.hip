@@ -564,7 +564,7 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
     }
 
     if (S <= kBk1MaxPairs && E <= kBk1MaxExperts) {
-        launch(pf, kStBucket, bucket_single_kernel, dim3(1), dim3(kBk1Waves * 64), st, idx, S, E, w.counts, w.offsets,
+        launch(pf, kStBucket, E <= 255 ? bucket_single_kernel<8> : bucket_single_kernel<9>, dim3(1), dim3(kBk1Waves * 64), st, idx, S, E, w.counts, w.offsets,
                w.entries, w.pos, w.tiles, w.big_tiles, w.n_tiles);
     } else {
         const int nchunks = bucket_chunks(S);
