@@ -87,7 +87,8 @@ struct GemmShape {
     static constexpr int BLoads = CW;                       // each wave loads its own groups
     static constexpr int HdrBuf = Groups * 256;             // headers of one super-block
     // headers move as 16-byte loads where they split evenly over the waves,
-    // else as 4-byte loads (a 16 x 128 tile's 2 KB over 4 waves)
+    // else as 4-byte loads (a 16 x 128 tile's 2 KB over 4 waves, a 64 x 256
+    // tile's 4 KB over 8)
     static constexpr int HdrLoadB = HdrBuf % (NW * 1024) == 0 ? 16 : 4;
     static constexpr int HdrLoads = HdrBuf / (NW * 64 * HdrLoadB);  // header loads per lane
     // k-step sums, 32 B per row: 8 waves, or 4 waves on 16-row tiles, load 4
@@ -360,24 +361,34 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     // scheduling pattern of a half (2*RB*CW MFMAs): its LDS reads early, two
     // per MFMA, then the unpack VALU spread over the rest, and nld global->LDS
     // loads spread evenly among those MFMAs so that the load pipe is fed
-    // steadily instead of in one burst (masks: 0x100 LDS read, 0x008 MFMA,
-    // 0x002 VALU, 0x020 global load)
+    // steadily instead of in one burst: one after every (slots / nld)-th MFMA,
+    // or, with more loads than MFMAs left (16-row and Q8 tiles), ceil(nld /
+    // slots) after each (masks: 0x100 LDS read, 0x008 MFMA, 0x002 VALU, 0x020
+    // global load)
     auto interleave = [&](int nld) {
         constexpr int kM = (Q8 ? 1 : 2) * RB * CW;
         constexpr int kDs0 = ((Q8 ? 1 : 2) * RB + CW + 1) / 2;
         constexpr int kDs = kDs0 < kM ? kDs0 : kM - 1;  // at least one MFMA left for the VALU groups
-        constexpr int kValuPer = (CW * 10 + (kM - kDs) - 1) / (kM - kDs) + 1;
-        const int every = nld > 0 ? (kM - kDs) / nld : kM;
+        constexpr int kSlots = kM - kDs;
+        constexpr int kValuPer = (CW * 10 + kSlots - 1) / kSlots + 1;
+        constexpr int kMaxPer = 16;  // bound on loads per slot (nld <= 16 on every shape)
+        const int every = nld > kSlots ? 1 : (nld > 0 ? kSlots / nld : kSlots);
+        const int per = nld > kSlots ? (nld + kSlots - 1) / kSlots : 1;
 #pragma unroll
         for (int i = 0; i < kDs; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
 #pragma unroll
-        for (int i = 0; i < kM - kDs; ++i) {
+        for (int i = 0; i < kSlots; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, kValuPer, 0);
-            if (nld > 0 && i % every == every - 1 && i / every < nld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (nld > 0 && i % every == every - 1) {
+                const int first = (i / every) * per;
+#pragma unroll
+                for (int c = 0; c < kMaxPer; ++c)
+                    if (c < per && first + c < nld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         }
     };
     // the B fragments unpacked in a half must exist at its end (the compiler
@@ -582,9 +593,12 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 // tiles_x * ncb units (tile, column block of 2*16 weight groups at 8 waves),
 // run one per CU, C CUs at a time; n_x % C units would make a last round that
 // leaves most of the XCD idle. When those r_x units fit C as halves (2 r_x <=
-// C), the launch skips them (mode 1) and a second launch of the 4-wave
-// instance runs each as two independent half-width units (mode 2), so the
-// last round is half as long; outputs do not overlap, nothing is summed.
+// C), the launch skips them (mode 1) and a second launch runs each as two
+// independent half-width units (mode 2: 64 x 256 tiles of 8 waves, each wave
+// 64 x 32, two per SIMD like the main launch; a 4-wave 64 x 256 instance, one
+// wave per SIMD, took 35 against 31 us for the 30b prefill's gate/up halves),
+// so the last round is about half as long; outputs do not overlap, nothing
+// is summed.
 struct TailSplit {
     int per_xcd;  // tiles per XCD (a contiguous range of the tile list)
     int full_x;   // units the main launch runs
@@ -627,7 +641,7 @@ __global__ __launch_bounds__(64 * NW, 1) __attribute__((
     float *svbuf = (float *)(smem + Sh::SvOff);
 
     // unit of this workgroup (tail_split): mode 0 every unit of this launch,
-    // 1 all but the XCD's split tail units, 2 (the 4-wave instance) the
+    // 1 all but the XCD's split tail units, 2 (the half-width instance) the
     // halves of the 8-wave launch's split units
     const int ntl = *n_tiles;
     const int x = blockIdx.x & 7, sid = blockIdx.x >> 3;

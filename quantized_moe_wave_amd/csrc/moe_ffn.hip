@@ -395,14 +395,16 @@ bool fold_norm_general(const moe_ffn_shape &s, int T) {
 // Dynamic LDS limits of the grouped GEMM instances (above the default).
 template <bool Q8>
 hipError_t gemm_lds_limits() {
-    const hipError_t a[6] = {
+    const hipError_t a[7] = {
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 2, 8, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 2, 8, Q8>::Lds),
+        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 2, 8, Q8>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 2, 8, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 8, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4, Q8>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
-        hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 4, 4, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 2, 4, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 2, 4, Q8>::Lds),
@@ -432,8 +434,10 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     using Small = GemmShape<1, 2, 4, Q8>;
     using Big = GemmShape<4, 4, 8, Q8>;
     using BigN = GemmShape<4, 4, 4, Q8>;
+    using Tail8 = GemmShape<4, 2, 8, Q8>;
     // big tiles: the 8-wave launch leaves each XCD's split tail units (see
-    // tail_split in gemm.hpp) to a 4-wave launch that runs them as halves;
+    // tail_split in gemm.hpp) to a second 8-wave launch that runs them as
+    // 64 x 256 halves (each wave 64 x 32, two waves per SIMD);
     // only where there are enough pairs for several big tiles per XCD (with
     // few or none the extra launch costs more than it saves)
     const int C = S >= (size_t)E * kGemmMinRows ? h->cus_per_xcd : 0;
@@ -446,7 +450,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
                    dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
                    w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
         if (C > 0)
-            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 4, 4, Q8>, dim3(8 * C), dim3(256), BigN::Lds, st,
+            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Tail8::Lds, st,
                        h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
                        w.h, I, C, 2);
     }
@@ -463,7 +467,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
                        dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
                        w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, C, 1);
             if (C > 0)
-                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 4, 4, Q8>, dim3(8 * C), dim3(256), BigN::Lds,
+                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Tail8::Lds,
                            st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs,
                            w.h_sinv, w.Y, H, C, 2);
         } else {

@@ -44,10 +44,11 @@ def shape(RB, CW, NW, Q8=False):
 
 
 # (RB, CW, NW, Q8, workgroups per CU the kernel is sized for): the big tiles
-# (64 x 512, 8 waves; 64 x 256, 4 waves) run one per CU, the 16 x 128 small
-# tiles four (three with the Q8 row scales)
-SHAPES = [(4, 4, 8, False, 1), (4, 4, 4, False, 1), (1, 2, 4, False, 4),
-          (4, 4, 8, True, 1), (4, 4, 4, True, 1), (1, 2, 4, True, 3)]
+# (64 x 512, 8 waves; 64 x 256, 4 waves where the weight groups do not split
+# into blocks of 32; 64 x 256, 8 waves for the last round's halves) run one
+# per CU, the 16 x 128 small tiles four (three with the Q8 row scales)
+SHAPES = [(4, 4, 8, False, 1), (4, 4, 4, False, 1), (4, 2, 8, False, 1), (1, 2, 4, False, 4),
+          (4, 4, 8, True, 1), (4, 4, 4, True, 1), (4, 2, 8, True, 1), (1, 2, 4, True, 3)]
 
 
 @pytest.mark.parametrize("RB,CW,NW,Q8,per_cu", SHAPES)
@@ -103,3 +104,36 @@ def test_lds_budget(RB, CW, NW, Q8, per_cu):
         assert sh["lds"] * (per_cu + 1) > LDS_PER_CU, "exactly that many fit (the register budget assumes it)"
     assert sh["abuf"] % (NW * 1024) == 0
     assert sh["M"] * sh["out_ld"] * 4 <= sh["sv_off"], "output staging must fit below the 1/s copies"
+
+
+def load_schedule(RB, CW, NW, Q8, nld):
+    """gemm_mainloop's interleave restated: global->LDS loads placed after each
+    MFMA slot of a half (the MFMAs left after the LDS-read group)."""
+    k_m = (1 if Q8 else 2) * RB * CW
+    k_ds0 = ((1 if Q8 else 2) * RB + CW + 1) // 2
+    k_ds = k_ds0 if k_ds0 < k_m else k_m - 1
+    slots = k_m - k_ds
+    every = 1 if nld > slots else (slots // nld if nld > 0 else slots)
+    per = (nld + slots - 1) // slots if nld > slots else 1
+    assert slots >= 1 and every >= 1 and per <= 16
+    placed = []
+    for i in range(slots):
+        n = 0
+        if nld > 0 and i % every == every - 1:
+            first = (i // every) * per
+            n = sum(1 for c in range(16) if c < per and first + c < nld)
+        placed.append(n)
+    return placed
+
+
+@pytest.mark.parametrize("RB,CW,NW,Q8,per_cu", SHAPES)
+def test_load_schedule(RB, CW, NW, Q8, per_cu):
+    # the load counts of the main loop's issue groups: HX + A (q == 0), A
+    # (q == 2), Bq + A (odd q), none (the last super-block's iterations)
+    sh = shape(RB, CW, NW, Q8)
+    a_loads = sh["abuf"] // (NW * 1024)
+    hx_loads = sh["hdr_loads"] + 1 + (1 if Q8 else 0)
+    for nld in (0, hx_loads + a_loads, a_loads, CW + a_loads):
+        placed = load_schedule(RB, CW, NW, Q8, nld)
+        assert sum(placed) == nld, "every load of the group must be placed once"
+        assert max(placed) <= -(-nld // len(placed)), "loads spread evenly over the slots"
