@@ -114,10 +114,10 @@ struct GemmShape {
 };
 constexpr int kGemmM = 64;  // rows of a big tile
 
-// Waves of a big-tile workgroup over ngroups weight groups (a multiple of 16:
-// I/8 for gate/up, H/16 for down): 8 (64 x 512 tiles) where the groups split
-// into blocks of 32, else 4 (64 x 256).
-__host__ __device__ inline int gemm_big_waves(int ngroups) { return ngroups % 32 == 0 ? 8 : 4; }
+// Weight groups per big tile over ngroups groups (a multiple of 16: I/8 for
+// gate/up, H/16 for down): 32 (64 x 512 tiles) where the groups split into
+// blocks of 32, else 16 (64 x 256; both 8 waves).
+__host__ __device__ inline int gemm_big_groups(int ngroups) { return ngroups % 32 == 0 ? 32 : 16; }
 
 // Upper bound on 64-row tiles for S bucket entries over E experts: each bucket
 // of c >= kGemmMinRows entries takes ceil(c / kGemmM) <= c / kGemmM + 1 tiles.

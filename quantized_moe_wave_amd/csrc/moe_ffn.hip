@@ -395,7 +395,7 @@ bool fold_norm_general(const moe_ffn_shape &s, int T) {
 // Dynamic LDS limits of the grouped GEMM instances (above the default).
 template <bool Q8>
 hipError_t gemm_lds_limits() {
-    const hipError_t a[7] = {
+    const hipError_t a[6] = {
         hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 4, 2, 8, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 2, 8, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 2, 8, Q8>,
@@ -404,8 +404,6 @@ hipError_t gemm_lds_limits() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 8, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 8, Q8>::Lds),
-        hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 4, 4, 4, Q8>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<4, 4, 4, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<true, 1, 2, 4, Q8>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<1, 2, 4, Q8>::Lds),
         hipFuncSetAttribute((const void *)expert_gemm_kernel<false, 1, 2, 4, Q8>,
@@ -427,14 +425,13 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
     // Grouped GEMM grids: 8 XCD lanes x column blocks x ceil(max tiles / 8)
     // (see gemm.hpp); 16-row x 128-column tiles (4 waves, four workgroups per
     // CU) for buckets of at most 16 entries, 64-row x 512-column tiles (8
-    // waves) for larger ones, or 64 x 256 (4 waves) where the weight groups do
-    // not split into blocks of 32.
+    // waves of 64 x 64) for larger ones, or 64 x 256 (8 waves of 64 x 32)
+    // where the weight groups do not split into blocks of 32.
     const int gu_groups = I / 8, dn_groups = H / kRowGroup;
     const int ms8 = (max_small_tiles(S, E) + 7) / 8, mg8 = (max_gemm_tiles(S, E) + 7) / 8;
     using Small = GemmShape<1, 2, 4, Q8>;
     using Big = GemmShape<4, 4, 8, Q8>;
-    using BigN = GemmShape<4, 4, 4, Q8>;
-    using Tail8 = GemmShape<4, 2, 8, Q8>;
+    using Half = GemmShape<4, 2, 8, Q8>;
     // big tiles: the 8-wave launch leaves each XCD's split tail units (see
     // tail_split in gemm.hpp) to a second 8-wave launch that runs them as
     // 64 x 256 halves (each wave 64 x 32, two waves per SIMD);
@@ -450,7 +447,7 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
                    dim3(512), Big::Lds, st, h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k,
                    w.x_hilo, w.x_xs, w.x_sinv, w.h, I, C, 1);
         if (C > 0)
-            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Tail8::Lds, st,
+            launch_lds(pf, kStGateUpTail, expert_gemm_kernel<true, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Half::Lds, st,
                        h->gu, gu_groups, nh, w.big_tiles, w.n_tiles + 1, w.entries, k, w.x_hilo, w.x_xs, w.x_sinv,
                        w.h, I, C, 2);
     }
@@ -462,17 +459,17 @@ void expert_gemms(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, hipStream_
                dim3(256), Small::Lds, st, h->dn, dn_groups, ni, w.tiles, w.n_tiles, w.entries, k, w.h_hilo,
                w.h_xs, w.h_sinv, w.Y, H, 0, 0);
     if (big) {
-        if (gemm_big_waves(dn_groups) == 8) {
+        if (gemm_big_groups(dn_groups) == Big::Groups) {
             launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 8, Q8>,
                        dim3(8 * (dn_groups / Big::Groups) * mg8), dim3(512), Big::Lds, st, h->dn, dn_groups, ni,
                        w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, C, 1);
             if (C > 0)
-                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Tail8::Lds,
+                launch_lds(pf, kStDownTail, expert_gemm_kernel<false, 4, 2, 8, Q8>, dim3(8 * C), dim3(512), Half::Lds,
                            st, h->dn, dn_groups, ni, w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs,
                            w.h_sinv, w.Y, H, C, 2);
         } else {
-            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 4, 4, Q8>,
-                       dim3(8 * (dn_groups / BigN::Groups) * mg8), dim3(256), BigN::Lds, st, h->dn, dn_groups, ni,
+            launch_lds(pf, kStDownBig, expert_gemm_kernel<false, 4, 2, 8, Q8>,
+                       dim3(8 * (dn_groups / Half::Groups) * mg8), dim3(512), Half::Lds, st, h->dn, dn_groups, ni,
                        w.big_tiles, w.n_tiles + 1, w.entries, k, w.h_hilo, w.h_xs, w.h_sinv, w.Y, H, 0, 0);
         }
     }

@@ -1,9 +1,10 @@
 """Coverage of the grouped GEMM's work split (CPU only).
 
 The big-tile GEMM launches of one projection split their units (expert tile,
-block of weight groups) between an 8-wave launch and, for each XCD's last
-round when it fits the XCD's compute units as halves, a 4-wave launch that runs
-each such unit as two half-width units. This test restates the kernel's unit
+block of 32 weight groups) between a launch of 64 x 512 tiles and, for each
+XCD's last round when it fits the XCD's compute units as halves, a launch of
+64 x 256 tiles that runs each such unit as two half-width units (where the
+weight groups do not split into blocks of 32, one launch of 64 x 256 tiles). This test restates the kernel's unit
 decode (expert_gemm_kernel's prologue and tail_split in gemm.hpp) and the
 host's launch choices (forward_layer in moe_ffn.hip) in Python, enumerates
 every workgroup of the launches, and checks that every (tile, weight group) of
@@ -18,8 +19,8 @@ import synth
 
 GEMM_M = 64            # rows of a big tile
 GEMM_MIN_ROWS = 17     # buckets of at least this many pairs take big tiles
-GROUPS_8W = 32         # weight groups of an 8-wave unit (64 x 512)
-GROUPS_4W = 16         # weight groups of a 4-wave unit (64 x 256)
+GROUPS_FULL = 32       # weight groups of a 64 x 512 unit
+GROUPS_HALF = 16       # weight groups of a 64 x 256 unit
 
 
 def tail_split(ntl, ncb, x, C):
@@ -63,12 +64,12 @@ def big_launches(ntl, S, E, ngroups, cus_per_xcd):
     """The host's big-tile launches of one projection: [(groups per unit, grid, mode, C)]."""
     C = cus_per_xcd if S >= E * GEMM_MIN_ROWS else 0
     mg8 = (max_gemm_tiles(S, E) + 7) // 8
-    if ngroups % 32 == 0:  # 8-wave instance
-        ls = [(GROUPS_8W, 8 * (ngroups // GROUPS_8W) * mg8, 1, C)]
+    if ngroups % 32 == 0:  # 64 x 512 tiles, the last round's split units as halves
+        ls = [(GROUPS_FULL, 8 * (ngroups // GROUPS_FULL) * mg8, 1, C)]
         if C > 0:
-            ls.append((GROUPS_4W, 8 * C, 2, C))
+            ls.append((GROUPS_HALF, 8 * C, 2, C))
         return ls
-    return [(GROUPS_4W, 8 * (ngroups // GROUPS_4W) * mg8, 0, 0)]
+    return [(GROUPS_HALF, 8 * (ngroups // GROUPS_HALF) * mg8, 0, 0)]
 
 
 def check_cover(ntl, S, E, ngroups, cus_per_xcd):
@@ -122,5 +123,5 @@ def test_workload_routings(name):
     if name == "30b-prefill":
         # the case that mixes both modes: with 274 tiles, XCDs 0-6 (35 tiles x 3 column blocks = 105 units on 32
         # CUs) split a last round of 9 units into halves, XCD 7 (29 tiles, 87 units) leaves its 23 whole
-        split = [tail_split(ntl, wl.inter // 8 // GROUPS_8W, x, 32)[2] for x in range(8)]
+        split = [tail_split(ntl, wl.inter // 8 // GROUPS_FULL, x, 32)[2] for x in range(8)]
         assert ntl == 274 and split == [9] * 7 + [0], (ntl, split)
