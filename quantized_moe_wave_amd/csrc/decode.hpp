@@ -57,6 +57,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *red, int *total)
 // norm_w (the block's RMSNorm weight, or null): x holds the residual stream
 // and every value is used normalised, fp32(x * norm_w * inv_rms), each wave
 // computing the 1/rms of the rows it reads (row_inv_rms).
+template <int TT>
 __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, const float *__restrict__ wr,
                                                   const float *__restrict__ bias, int T, int H, int E,
                                                   double *__restrict__ logits, f16 *__restrict__ x_hilo,
@@ -75,25 +76,26 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                      x_sinv + (size_t)t * nsb, -10000, norm_w, ir, q8 != 0);
     }
 
-    // Loads are unconditional (chunk and token indices clamped) so that all of
-    // a wave's loads are in flight together; out-of-range terms are skipped.
+    // Loads are unconditional (chunk indices clamped) so that all of a wave's
+    // loads are in flight together; out-of-range terms are skipped. TT = T
+    // (one instance per token count): no wave loads a row twice.
     for (int e = blockIdx.x * wpb + wave; e < E; e += nw) {
-        double acc[kSmallT];
+        double acc[TT];
 #pragma unroll
-        for (int t = 0; t < kSmallT; ++t) acc[t] = 0.0;
+        for (int t = 0; t < TT; ++t) acc[t] = 0.0;
         // 1/rms of each token's row: from the chunk registers below when the
         // whole row fits one pass of them (nsb <= 8), else read ahead here
         const bool rms_ahead = norm_w && nsb > 8;
-        double ir[kSmallT];
+        double ir[TT];
 #pragma unroll
-        for (int t = 0; t < kSmallT; ++t) ir[t] = (rms_ahead && t < T) ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
+        for (int t = 0; t < TT; ++t) ir[t] = (rms_ahead && t < T) ? row_inv_rms(x + (size_t)t * H, H, eps) : 1.0;
         const float *wrow = wr + (size_t)e * H;
         for (int c0 = 0; c0 < nsb; c0 += 8) {
-            float4 wv[8], xv[kSmallT][8];
+            float4 wv[8], xv[TT][8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) wv[i] = *(const float4 *)(wrow + min(c0 + i, nsb - 1) * kQ4Weights + lane * 4);
 #pragma unroll
-            for (int t = 0; t < kSmallT; ++t)
+            for (int t = 0; t < TT; ++t)
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     xv[t][i] = *(const float4 *)(x + (size_t)min(t, T - 1) * H + min(c0 + i, nsb - 1) * kQ4Weights +
@@ -104,7 +106,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                 for (int i = 0; i < 8; ++i) gv[i] = *(const float4 *)(norm_w + min(c0 + i, nsb - 1) * kQ4Weights + lane * 4);
                 if (!rms_ahead) {
 #pragma unroll
-                    for (int t = 0; t < kSmallT; ++t) {
+                    for (int t = 0; t < TT; ++t) {
                         if (t < T) {
                             double ss = 0.0;
 #pragma unroll
@@ -123,7 +125,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
 #pragma unroll
-                    for (int t = 0; t < kSmallT; ++t) {
+                    for (int t = 0; t < TT; ++t) {
                         if (t >= T) continue;
                         const float4 g4 = gv[i];
                         xv[t][i].x = (float)((double)xv[t][i].x * g4.x * ir[t]);
@@ -134,7 +136,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
                 }
             }
 #pragma unroll
-            for (int t = 0; t < kSmallT; ++t) {
+            for (int t = 0; t < TT; ++t) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     if (t < T && c0 + i < nsb) {
@@ -149,7 +151,7 @@ __device__ __forceinline__ void logits_small_body(const float *__restrict__ x, c
             }
         }
 #pragma unroll
-        for (int t = 0; t < kSmallT; ++t) {
+        for (int t = 0; t < TT; ++t) {
             if (t < T) {
                 double s = wave_sum(acc[t]);
                 if (lane == 0) {
@@ -291,12 +293,13 @@ __device__ __forceinline__ void routing_outputs_small(const double *logits, int 
 // is recomputed from the logits by every workgroup of the next two launches
 // (each needs only its own token's choice), which is cheaper than handing the
 // choice from workgroup to workgroup.
+template <int TT>
 __global__ __launch_bounds__(64) void router_small_kernel(const float *__restrict__ x, const float *__restrict__ wr,
                                                            const float *__restrict__ bias, int T, int H, int E,
                                                            double *__restrict__ logits, f16 *__restrict__ x_hilo,
                                                            f16 *__restrict__ x_xs, float *__restrict__ x_sinv,
                                                            const float *__restrict__ norm_w, double eps, int q8) {
-    logits_small_body(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv, norm_w, eps, q8);
+    logits_small_body<TT>(x, wr, bias, T, H, E, logits, x_hilo, x_xs, x_sinv, norm_w, eps, q8);
 }
 
 constexpr int kSmallMaxH = 4096;  // hidden sizes the small path stages in LDS

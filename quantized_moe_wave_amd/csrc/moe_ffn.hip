@@ -498,7 +498,9 @@ moe_status forward_layer(moe_ffn_t h, Workspace &w, Profiler &pf, int32_t T, con
         return fail(MOE_ERR_INVALID_ARG, "internal: fused norm where the router cannot take it");
     if (decode_path(s, T)) {
         // decode path: three launches (see decode.hpp)
-        launch(pf, kStRouter, router_small_kernel, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
+        auto rk = T == 1 ? router_small_kernel<1> : T == 2 ? router_small_kernel<2> : T == 3 ? router_small_kernel<3>
+                                                                                       : router_small_kernel<4>;
+        launch(pf, kStRouter, rk, dim3(E + T * nh), dim3(64), st, x, h->rw, h->rb, T, H, E,
                w.logits, w.x_hilo, w.x_xs, w.x_sinv, norm_w, eps, q8);
         launch(pf, kStGateUp, gateup_pair_kernel, dim3(S, I / 8), dim3(kGpWaves * 64), st, h->gu, I / 8, nh, w.logits, E, k,
                w.x_hilo, w.x_xs, w.x_sinv, w.h, I, w.dsel, w.dw);
