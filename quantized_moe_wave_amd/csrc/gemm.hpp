@@ -19,7 +19,9 @@
 // only its min term: its B is zeroed and its d taken as 1 in both ratios.
 // Each rescale costs one fp32 rounding, far below the 1e-4 bar over a few
 // dozen super-blocks. One accumulator instead of a per-super-block partial
-// plus a running sum halves the accumulator registers.
+// plus a running sum halves the accumulator registers (64-row tiles; the
+// 16-row tiles of exact activations have registers to spare and use the
+// partial plus running sum, kTwoAcc below).
 //
 // Work split: a workgroup of NW waves owns a (16*RB) x (16*NW*CW) output
 // tile: up to 16*RB rows of one expert's bucket (the last tile of a bucket
@@ -344,8 +346,28 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) X[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // 16-row tiles (exact activations): the registers allow the plain form,
+    // each super-block's MFMA sum P in an accumulator of its own (started from
+    // zero by the super-block's first MFMA) and X += d_b P_b once it is
+    // complete (at the next super-block's start, and after the last); the
+    // min term goes into X as -dmin_b Q_b. No d ratio, reciprocal or rescale:
+    // ~9% of those tiles' VALU. 64-row tiles keep the rescaled single
+    // accumulator (two would not fit two waves per SIMD), Q8 tiles too (their
+    // row scales change per super-block).
+    constexpr bool kTwoAcc = RB == 1 && !Q8;
+    f32x4 P[CW];
+#pragma unroll
+    for (int cb = 0; cb < CW; ++cb) P[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto mfma_half = [&](const f16x8 (&Ah)[RB], const f16x8 (&Al)[RB], const f16x8 (&Bf)[CW]) {
+    auto mfma_half = [&](const f16x8 (&Ah)[RB], const f16x8 (&Al)[RB], const f16x8 (&Bf)[CW], bool first) {
+        if constexpr (kTwoAcc) {
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cb = 0; cb < CW; ++cb) P[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah[0], Bf[cb], first ? zero : P[cb], 0, 0, 0);
+#pragma unroll
+            for (int cb = 0; cb < CW; ++cb) P[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al[0], Bf[cb], P[cb], 0, 0, 0);
+            return;
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -449,10 +471,14 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
             const u32x4 hdr = *(const u32x4 *)(hb + cb * 256 + n * 16);
-            float d = half_bits_to_float(hdr.x & 0xFFFFu);
-            d = d != 0.f ? d : 1.f;
-            // reciprocal to 1 ulp: far below the bar, and no division sequence
-            r1[cb] = half_bits_to_float(hdr.x >> 16) * __builtin_amdgcn_rcpf(d);
+            if constexpr (kTwoAcc) {
+                r1[cb] = half_bits_to_float(hdr.x >> 16);  // X is in absolute units: -dmin Q
+            } else {
+                float d = half_bits_to_float(hdr.x & 0xFFFFu);
+                d = d != 0.f ? d : 1.f;
+                // reciprocal to 1 ulp: far below the bar, and no division sequence
+                r1[cb] = half_bits_to_float(hdr.x >> 16) * __builtin_amdgcn_rcpf(d);
+            }
             const uint32_t mn_lo = hdr.z & 0x3F3F3F3Fu;
             const uint32_t mn_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
             // this lane's mins 4(g%2) .. 4(g%2)+3 (a select of register
@@ -481,6 +507,10 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
         const uint8_t *hn = hbuf + ((b + 1) & 1) * Sh::HdrBuf + wave * CW * 256;
 #pragma unroll
         for (int cb = 0; cb < CW; ++cb) {
+            if constexpr (kTwoAcc) {  // d_b for the fold X += d_b P_b (d = 0 adds nothing)
+                fcur[cb] = half_bits_to_float(*(const uint32_t *)(hb + cb * 256 + n * 16) & 0xFFFFu);
+                continue;
+            }
             float d = half_bits_to_float(*(const uint32_t *)(hb + cb * 256 + n * 16) & 0xFFFFu);
             float dn = half_bits_to_float(*(const uint32_t *)(hn + cb * 256 + n * 16) & 0xFFFFu);
             d = d != 0.f ? d : 1.f;
@@ -519,17 +549,24 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                             fr[rb][i] = (dp[i] != 0.f ? dp[i] : 1.f) * __builtin_amdgcn_rcpf(dc[i] != 0.f ? dc[i] : 1.f);
                     }
                 }
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
+                if constexpr (kTwoAcc) {  // the previous super-block's sum (none before the first: P = 0)
 #pragma unroll
                     for (int cb = 0; cb < CW; ++cb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) X[rb][cb][i] *= Q8 ? fcur[cb] * fr[rb][i] : fcur[cb];
+                        for (int i = 0; i < 4; ++i) X[0][cb][i] = __builtin_fmaf(fcur[cb], P[cb][i], X[0][cb][i]);
+                } else {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int cb = 0; cb < CW; ++cb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) X[rb][cb][i] *= Q8 ? fcur[cb] * fr[rb][i] : fcur[cb];
+                }
             }
             if (q == 1) min_term(b);
             read_a_half(c, 1, Ah1, Al1);
             build_b_half(1, kp, wq, B1);
-            mfma_half(Ah0, Al0, B0);
+            mfma_half(Ah0, Al0, B0, q == 0);
             interleave(0);
             pin(B1);
             __builtin_amdgcn_sched_barrier(0);
@@ -578,7 +615,7 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
                 if (q & 1) issue_bq((c + 3) / 2);
                 issue_a(c + 4);
             }
-            mfma_half(Ah1, Al1, B1);
+            mfma_half(Ah1, Al1, B1, false);
             interleave(!LOADS ? 0 : q == 0 ? kHxLoads + kALoads : q == 2 ? kALoads : kBLoads + kALoads);
             pin(B0);
             __builtin_amdgcn_sched_barrier(0);
@@ -587,6 +624,14 @@ __device__ __forceinline__ void gemm_mainloop(uint8_t *__restrict__ abuf, uint8_
     for (int b = 0; b < nsb - 1; ++b) sb_step(b, std::integral_constant<bool, true>{});
     sb_step(nsb - 1, std::integral_constant<bool, false>{});
     wait_vm<0>();  // no load into LDS may still be in flight when the workgroup ends
+    if constexpr (kTwoAcc) {  // the last super-block's sum; the epilogue's factor is then 1
+#pragma unroll
+        for (int cb = 0; cb < CW; ++cb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X[0][cb][i] = __builtin_fmaf(fcur[cb], P[cb][i], X[0][cb][i]);
+            fcur[cb] = 1.f;
+        }
+    }
 }
 
 // Last-round balance of a big-tile launch. Per XCD x the launch has n_x =
