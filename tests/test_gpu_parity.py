@@ -3,8 +3,9 @@
 Every workload at its full size, every output element of every token compared
 with the oracle (the two large ones also have a fast sampled variant). Edge
 cases: ragged token counts across tile boundaries, one
-expert taking every token, k = E, zero input, wide dynamic range, workspace
-growth, bitwise run-to-run determinism, and the ABI's error returns.
+expert taking every token, k = E, zero input, wide dynamic range, Q4_K
+super-blocks with d = 0 (on 16-row and 64-row tiles), workspace growth,
+bitwise run-to-run determinism, and the ABI's error returns.
 """
 import numpy as np
 import pytest
@@ -360,3 +361,29 @@ def test_decode_odd_unit_counts(k, inter):
     xn = oracle.rms_norm(hidden, gn, synth.NORM_EPS).astype(np.float32)
     parity.check_parity(synth.LayerInputs(wl.with_tokens(T), xn, inp.router, inp.bias, inp.gate, inp.up, inp.down), run,
                         resid=hidden)
+
+
+@pytest.mark.parametrize("name,T", [("30b-batch", 64), ("tiny", 200)])
+def test_super_blocks_with_zero_d(name, T):
+    # Q4_K super-blocks whose d is 0 (scales, quants, dmin and mins left as
+    # generated): such a block's weights are -dmin * m, only its min term
+    # counts. 30b-batch at 64 tokens runs every bucket on 16-row tiles (each
+    # super-block's sum in its own accumulator), tiny at 200 tokens on 64-row
+    # tiles (the rescaled accumulator, whose d ratios treat d = 0 as 1)
+    print(f"[parity] {name} T={T}: every third super-block with d = 0", flush=True)
+    import torch
+
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl, seed=4)
+    for m in (inp.gate, inp.up, inp.down):
+        blocks = m.reshape(-1, synth.Q4K_BLOCK_BYTES)
+        blocks[::3, 0:2] = 0
+    _cache.clear()
+    layer, _ = parity.make_layer(inp)
+    try:
+        x = synth.gen_x(4, 7, T, wl.hidden).astype(np.float32)
+        inp2 = synth.LayerInputs(wl.with_tokens(T), x, inp.router, inp.bias, inp.gate, inp.up, inp.down)
+        g = parity.run_gpu(layer, torch.from_numpy(x).cuda())
+        parity.check_parity(inp2, g)
+    finally:
+        layer.close()
